@@ -1,0 +1,126 @@
+"""CPU oracle for the MoE finalize path and the two sibling fused norms.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg
+of ``bench.py`` are the only callers.  The product path never imports this package, and
+this package imports nothing from the GPU library.
+
+The arithmetic lives in ``oracle.c`` (plain loops; FP32 FMA where the pages fix the
+precision, float64 everywhere else).  This module compiles it with gcc when the shared
+object is missing or older than its source, and wraps it for numpy arrays.
+bfloat16 arrays are ``numpy.uint16`` bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_DIR, "oracle.c")
+LIB = os.path.join(_DIR, "liboracle.so")
+# No fast-math and no contraction: every FMA in the source is an explicit fmaf().
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+          "-Wall", "-Wextra"]
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc; returns the library path."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", *CFLAGS, "-o", tmp, SRC, "-lm"], check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        p, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+        lib.oracle_moe_finalize.argtypes = [p, i64, p, p, p, p, i32, p, p, p, f32, p, i64, i32, i32]
+        lib.oracle_gated_residual_rmsnorm.argtypes = [p, p, p, p, p, f32, p, i64, i32]
+        lib.oracle_rmsnorm_sigmoid_gate.argtypes = [p, p, p, f32, p, i64, i32, i32]
+        lib.oracle_bf16_round.argtypes = [p, p, i64]
+        lib.oracle_bf16_round.restype = None
+        _lib = lib
+    return _lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def moe_finalize(expert_rows, idx, weights, residual, gamma, eps, expert_ids=None,
+                 expert_gamma=None):
+    """Return (residual_out float32 [T,H], out bf16-bits [T,H]).
+
+    expert_rows: bf16 [num_rows, H]; idx: int32 [T, k]; weights: float32 [T, k];
+    residual: float32 [T, H]; gamma: bf16 [H]; expert_ids: int32 [T, k] and
+    expert_gamma: bf16 [E, H] together select the per-expert RMSNorm variant.
+    """
+    lib = _load()
+    rows, prows = _c(expert_rows, np.uint16)
+    idx, pidx = _c(idx, np.int32)
+    w, pw = _c(weights, np.float32)
+    res, pres = _c(residual, np.float32)
+    g, pg = _c(gamma, np.uint16)
+    T, k = idx.shape
+    H = rows.shape[1]
+    if (expert_ids is None) != (expert_gamma is None):
+        raise ValueError("expert_ids and expert_gamma go together")
+    pe = pge = None
+    E = 0
+    if expert_gamma is not None:
+        eids, pe = _c(expert_ids, np.int32)
+        ge, pge = _c(expert_gamma, np.uint16)
+        E = ge.shape[0]
+    r_out = np.empty((T, H), dtype=np.float32)
+    out = np.empty((T, H), dtype=np.uint16)
+    st = lib.oracle_moe_finalize(prows, rows.shape[0], pidx, pw, pe, pge, E, pres,
+                                 r_out.ctypes.data_as(ctypes.c_void_p), pg, float(eps),
+                                 out.ctypes.data_as(ctypes.c_void_p), T, H, k)
+    if st != 0:
+        raise ValueError(f"oracle_moe_finalize failed with status {st}")
+    return r_out, out
+
+
+def gated_residual_rmsnorm(x, gate, residual, gamma, eps):
+    """Return (residual_out float32 [T,H], out bf16-bits [T,H])."""
+    lib = _load()
+    x, px = _c(x, np.uint16)
+    gt, pgt = _c(gate, np.uint16)
+    res, pres = _c(residual, np.float32)
+    g, pg = _c(gamma, np.uint16)
+    T, H = x.shape
+    r_out = np.empty((T, H), dtype=np.float32)
+    out = np.empty((T, H), dtype=np.uint16)
+    lib.oracle_gated_residual_rmsnorm(px, pgt, pres, r_out.ctypes.data_as(ctypes.c_void_p), pg,
+                                      float(eps), out.ctypes.data_as(ctypes.c_void_p), T, H)
+    return r_out, out
+
+
+def rmsnorm_sigmoid_gate(x, gate, gamma, eps):
+    """Return out bf16-bits with the shape of x ([T, heads, D])."""
+    lib = _load()
+    x, px = _c(x, np.uint16)
+    gt, pgt = _c(gate, np.uint16)
+    g, pg = _c(gamma, np.uint16)
+    T, heads, D = x.shape
+    out = np.empty_like(x)
+    lib.oracle_rmsnorm_sigmoid_gate(px, pgt, pg, float(eps), out.ctypes.data_as(ctypes.c_void_p),
+                                    T, heads, D)
+    return out
+
+
+def bf16_round(v):
+    """Round float64 values to bfloat16 bit patterns (nearest, ties to even)."""
+    lib = _load()
+    v, pv = _c(v, np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib.oracle_bf16_round(pv, out.ctypes.data_as(ctypes.c_void_p), v.size)
+    return out

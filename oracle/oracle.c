@@ -1,0 +1,192 @@
+/*
+ * Plain CPU oracle for the MoE finalize path and its two sibling fused norms.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark may load this library.  It shares no code, header, table or helper with
+ * the GPU library; the two are independent implementations of the same definitions.
+ *
+ * Every function is the plain definition, written out with one loop per step and no
+ * blocking, fusion or reordering:
+ *
+ *  - The weighted accumulation is the one place where the pages fix the precision: the
+ *    deterministic finalize (page "FlashInfer MoE performance: improving the deterministic
+ *    finalize with CuTe DSL", PR #5319, section 1, the _fma_rn listing and the paragraph
+ *    after it) accumulates the gathered expert rows with FP32 fused multiply-adds, rounded
+ *    to nearest, in a fixed order, and converts to BF16 only at the end.  Here that is
+ *    fmaf() for j = 0..k-1, starting from +0.  The flush-to-zero in that listing is there to
+ *    match an older fast-math kernel and only changes values below 2^-126; this oracle
+ *    keeps denormals.
+ *  - The residual add is one float32 addition after the k-term sum (page "MoE all-reduce
+ *    fusion for Blackwell: FlashInfer's Cake backend", PR #4730, section 2, fusion
+ *    strategy: the expert outputs are summed, the residual added and RMSNorm applied in one
+ *    launch; the residual stream stays FP32 per page "FlashInfer fused norms and TP/EP MoE
+ *    for Muse-Spark-Open", PR #6544, section 1.1).
+ *  - Everything the pages leave open is computed in float64: sums of squares, the RMSNorm
+ *    scale (mean(x^2) + eps)^-1/2, the sigmoid 1/(1+e^-g), and products with gamma.  A
+ *    float64 value is rounded once, to nearest-even, to the stored type (float32 or bf16).
+ *
+ * bfloat16 values are passed as their raw 16-bit patterns.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Exact widening of a bfloat16 bit pattern: it is the upper half of a binary32. */
+static double bf16_value(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a float64 to the nearest bfloat16 (8 significant bits, ties to even), once. */
+static uint16_t bf16_round(double v) {
+    if (isnan(v)) return 0x7FC0;
+    if (v == 0.0) return signbit(v) ? 0x8000 : 0x0000;
+    double r;
+    if (fabs(v) < 0x1p-126) {
+        /* subnormal range of bfloat16: a fixed spacing of 2^-133 */
+        r = ldexp(nearbyint(ldexp(v, 133)), -133);
+    } else {
+        int e;
+        double m = frexp(v, &e);                      /* v = m * 2^e, 0.5 <= |m| < 1 */
+        r = ldexp(nearbyint(ldexp(m, 8)), e - 8);     /* keep 8 significant bits */
+    }
+    float f = (float)r; /* exact (8 significant bits), or +-inf past the bf16 range */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* RMSNorm scale of n values: (sum(x^2)/n + eps)^(-1/2), all in float64. */
+static double rms_scale_f32(const float* x, int64_t n, float eps) {
+    double ss = 0.0;
+    for (int64_t i = 0; i < n; ++i) ss += (double)x[i] * (double)x[i];
+    return 1.0 / sqrt(ss / (double)n + (double)eps);
+}
+
+static double rms_scale_bf16(const uint16_t* x, int64_t n, float eps) {
+    double ss = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double v = bf16_value(x[i]);
+        ss += v * v;
+    }
+    return 1.0 / sqrt(ss / (double)n + (double)eps);
+}
+
+static double sigmoid(double g) { return 1.0 / (1.0 + exp(-g)); }
+
+/*
+ * MoE finalize with a residual add and a final RMSNorm.
+ *
+ * For token t, slot j's expert output is row idx[t,j] of expert_rows, the permuted GEMM2
+ * output that the TP MoE finalize reads directly (PR #6544 page, section 2.1).  If
+ * expert_gamma is given, each gathered row is first RMSNormed over H with the gamma of its
+ * expert expert_ids[t,j] (the per-expert RMSNorm of that section); the normalised row is
+ * rounded to float32.  Then
+ *     acc = +0;  acc = fmaf(w[t,j], row_j, acc) for j = 0..k-1
+ *     residual_out[t] = residual[t] + acc                              (float32)
+ *     out[t] = bf16(residual_out[t] * rms_scale(residual_out[t]) * gamma)
+ *
+ * Returns 0, -1 if an index is out of range, -2 if scratch memory cannot be allocated.
+ * residual_out may be the same array as residual.
+ */
+int oracle_moe_finalize(const uint16_t* expert_rows, int64_t num_rows, const int32_t* idx,
+                        const float* weights, const int32_t* expert_ids,
+                        const uint16_t* expert_gamma, int32_t num_experts, const float* residual,
+                        float* residual_out, const uint16_t* gamma, float eps, uint16_t* out,
+                        int64_t T, int32_t H, int32_t k) {
+    float* acc = (float*)malloc(sizeof(float) * (size_t)(H > 0 ? H : 1));
+    float* row = (float*)malloc(sizeof(float) * (size_t)(H > 0 ? H : 1));
+    int status = 0;
+    if (!acc || !row) {
+        status = -2;
+        goto done;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < H; ++h) acc[h] = 0.0f;
+        for (int32_t j = 0; j < k; ++j) {
+            int64_t p = idx[t * k + j];
+            if (p < 0 || p >= num_rows) {
+                status = -1;
+                goto done;
+            }
+            const uint16_t* x = expert_rows + p * (int64_t)H;
+            if (expert_gamma) {
+                int32_t e = expert_ids[t * k + j];
+                if (e < 0 || e >= num_experts) {
+                    status = -1;
+                    goto done;
+                }
+                const uint16_t* ge = expert_gamma + (int64_t)e * H;
+                double s = rms_scale_bf16(x, H, eps);
+                for (int32_t h = 0; h < H; ++h)
+                    row[h] = (float)(bf16_value(x[h]) * s * bf16_value(ge[h]));
+            } else {
+                for (int32_t h = 0; h < H; ++h) row[h] = (float)bf16_value(x[h]);
+            }
+            float wj = weights[t * k + j];
+            for (int32_t h = 0; h < H; ++h) acc[h] = fmaf(wj, row[h], acc[h]);
+        }
+        const float* res = residual + t * (int64_t)H;
+        float* r = residual_out + t * (int64_t)H;
+        for (int32_t h = 0; h < H; ++h) r[h] = res[h] + acc[h];
+        double s = rms_scale_f32(r, H, eps);
+        uint16_t* o = out + t * (int64_t)H;
+        for (int32_t h = 0; h < H; ++h) o[h] = bf16_round((double)r[h] * s * bf16_value(gamma[h]));
+    }
+done:
+    free(acc);
+    free(row);
+    return status;
+}
+
+/*
+ * Gated-residual RMSNorm (PR #6544 page, section 1.1): gating, the residual add and
+ * RMSNorm in one pass over an FP32 residual stream.
+ *     residual_out = float32(residual + sigmoid(gate) * x)     (one rounding)
+ *     out = bf16(residual_out * rms_scale(residual_out) * gamma)
+ */
+int oracle_gated_residual_rmsnorm(const uint16_t* x, const uint16_t* gate, const float* residual,
+                                  float* residual_out, const uint16_t* gamma, float eps,
+                                  uint16_t* out, int64_t T, int32_t H) {
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t* xt = x + t * (int64_t)H;
+        const uint16_t* gt = gate + t * (int64_t)H;
+        const float* res = residual + t * (int64_t)H;
+        float* r = residual_out + t * (int64_t)H;
+        for (int32_t h = 0; h < H; ++h)
+            r[h] = (float)((double)res[h] + sigmoid(bf16_value(gt[h])) * bf16_value(xt[h]));
+        double s = rms_scale_f32(r, H, eps);
+        uint16_t* o = out + t * (int64_t)H;
+        for (int32_t h = 0; h < H; ++h) o[h] = bf16_round((double)r[h] * s * bf16_value(gamma[h]));
+    }
+    return 0;
+}
+
+/*
+ * Per-head RMSNorm with a sigmoid gate (same page, section 1.2): every head of every token
+ * is normalised over its D values with one gamma[D] shared by all heads, then multiplied by
+ * the sigmoid of the gate element.
+ *     out[t,n,d] = bf16(x[t,n,d] * rms_scale(x[t,n,:]) * gamma[d] * sigmoid(gate[t,n,d]))
+ */
+int oracle_rmsnorm_sigmoid_gate(const uint16_t* x, const uint16_t* gate, const uint16_t* gamma,
+                                float eps, uint16_t* out, int64_t T, int32_t num_heads,
+                                int32_t D) {
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t n = 0; n < num_heads; ++n) {
+            int64_t base = (t * num_heads + n) * (int64_t)D;
+            double s = rms_scale_bf16(x + base, D, eps);
+            for (int32_t d = 0; d < D; ++d)
+                out[base + d] = bf16_round(bf16_value(x[base + d]) * s * bf16_value(gamma[d]) *
+                                           sigmoid(bf16_value(gate[base + d])));
+        }
+    }
+    return 0;
+}
+
+/* Round float64 values to bfloat16 bit patterns; lets the tests pin the rounding itself. */
+void oracle_bf16_round(const double* v, uint16_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_round(v[i]);
+}

@@ -1,0 +1,370 @@
+"""Pins of the CPU oracle to facts outside itself (CPU only).
+
+Each test checks the oracle against something the pages or the mathematics fix: hand
+worked examples, float64 brute force written independently with numpy/scipy, closed forms,
+special cases that reduce to a library routine (torch's rms_norm, float32 addition), and
+invariants (permutation equivariance, exact power-of-two scaling).  The cases are chosen so
+that a plausible slip in the oracle (a dropped term, a wrong sign or index, a transposed
+operand, a wrong norm axis, a double rounding) fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit
+
+import oracle
+import workloads
+from tests.helpers import bf16_ulp_diff, f32, torch_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+U32 = 2.0 ** -24  # unit roundoff of float32
+
+
+def _bits(hexes):
+    return np.array([[int(h, 16) for h in row] for row in hexes], dtype=np.uint16)
+
+
+def _rows_bf16(values):
+    b = workloads.to_bf16_bits(np.asarray(values, dtype=np.float32))
+    assert np.array_equal(f32(b), np.asarray(values, dtype=np.float32)), "fixture not exact in bf16"
+    return b
+
+
+# ----------------------------------------------------------------------------- golden
+
+
+def test_golden_finalize_hand_example():
+    g = json.load(open(GOLDEN))["moe_finalize"]
+    r, o = oracle.moe_finalize(_rows_bf16(g["expert_rows"]), np.array(g["idx"], np.int32),
+                               np.array(g["weights"], np.float32),
+                               np.array(g["residual"], np.float32), _rows_bf16(g["gamma"]),
+                               g["eps"])
+    assert np.array_equal(r, np.array(g["expected_residual_out"], np.float32))
+    assert np.array_equal(o, _bits(g["expected_out_bits"]))
+
+
+def test_golden_gated_hand_example():
+    g = json.load(open(GOLDEN))["gated_residual_rmsnorm"]
+    r, o = oracle.gated_residual_rmsnorm(_rows_bf16(g["x"]), _rows_bf16(g["gate"]),
+                                         np.array(g["residual"], np.float32),
+                                         _rows_bf16(g["gamma"]), g["eps"])
+    assert np.array_equal(r, np.array(g["expected_residual_out"], np.float32))
+    assert np.array_equal(o, _bits(g["expected_out_bits"]))
+
+
+def test_golden_per_head_hand_example():
+    g = json.load(open(GOLDEN))["rmsnorm_sigmoid_gate"]
+    x = _rows_bf16(np.array(g["x"], np.float32).reshape(-1, g["D"])).reshape(np.shape(g["x"]))
+    gt = _rows_bf16(np.array(g["gate"], np.float32).reshape(-1, g["D"])).reshape(x.shape)
+    o = oracle.rmsnorm_sigmoid_gate(x, gt, _rows_bf16(g["gamma"]), g["eps"])
+    exp = np.array([[[int(h, 16) for h in head] for head in tok] for tok in g["expected_out_bits"]],
+                   dtype=np.uint16)
+    assert np.array_equal(o, exp)
+
+
+# ----------------------------------------------------------------------------- bf16 rounding
+
+
+def test_bf16_round_matches_torch_on_float32_values():
+    # On values that are exactly float32 there is only one rounding, so the oracle's
+    # double->bf16 rounding must agree bit for bit with torch's float32->bf16 cast (RNE).
+    rng = np.random.default_rng(11)
+    v = np.concatenate([rng.standard_normal(200000).astype(np.float32),
+                        (rng.standard_normal(20000) * 1e30).astype(np.float32),
+                        (rng.standard_normal(20000) * 1e-30).astype(np.float32)])
+    assert np.array_equal(oracle.bf16_round(v.astype(np.float64)), torch_bf16_bits(v))
+
+
+def test_bf16_round_special_cases():
+    cases = {
+        1.0: 0x3F80, -1.0: 0xBF80, 0.0: 0x0000,
+        1.0 + 2.0 ** -8: 0x3F80,          # tie between 1 and 1+2^-7: even mantissa (1) wins
+        1.0 + 3 * 2.0 ** -8: 0x3F82,      # tie between 1+2^-7 and 1+2^-6: even (1+2^-6) wins
+        1.0 + 2.0 ** -8 + 2.0 ** -40: 0x3F81,  # just above the tie: rounds up (no double rounding)
+        2.0 ** -130: 0x0008,              # bf16 subnormal, spacing 2^-133
+        3.0e38: 0x7F62, 3.5e38: 0x7F80,   # largest finite range, then overflow to +inf
+    }
+    for v, bits in cases.items():
+        assert oracle.bf16_round(np.array([v]))[0] == bits, (v, hex(bits))
+    assert oracle.bf16_round(np.array([-0.0]))[0] == 0x8000
+
+
+# ----------------------------------------------------------------------------- finalize
+
+
+def _bf_finalize(d):
+    """float64 brute force: residual + sum_j w * row[idx]."""
+    x = f32(d["expert_rows"]).astype(np.float64)
+    terms = d["weights"][..., None].astype(np.float64) * x[d["idx"]]
+    return d["residual"].astype(np.float64) + terms.sum(axis=1), np.abs(terms).sum(axis=1)
+
+
+def _close_bf16(a, b, min_exact=0.999):
+    """Within one bf16 ulp everywhere, and bit-identical almost everywhere (the reference
+    rounds float64 -> float32 -> bf16, so it may differ from a single rounding at ties)."""
+    d = bf16_ulp_diff(a, b)
+    return d.max() <= 1 and (d == 0).mean() >= min_exact
+
+
+def _rmsnorm_bits(r, gamma, eps):
+    """Textbook RMSNorm through torch (float64), then to bf16."""
+    rt = torch.from_numpy(np.asarray(r, np.float64))
+    y = torch.nn.functional.rms_norm(rt, (rt.shape[-1],), weight=torch.from_numpy(
+        f32(gamma).astype(np.float64)), eps=eps)
+    return torch_bf16_bits(y.numpy())
+
+
+@pytest.mark.parametrize("T,H,k,layout", [(1, 8, 1, "random"), (3, 24, 2, "random"),
+                                          (16, 1024, 8, "expert_sorted"), (5, 40, 3, "random"),
+                                          (7, 1024, 2, "expert_sorted")])
+def test_finalize_brute_force(T, H, k, layout):
+    d = workloads.make_finalize_inputs(T, H, E=max(8, k), k=k, seed=100 + T + H + k, layout=layout)
+    r, o = oracle.moe_finalize(d["expert_rows"], d["idx"], d["weights"], d["residual"],
+                               d["gamma"], d["eps"])
+    exact, mag = _bf_finalize(d)
+    bound = (k + 1) * U32 * (np.abs(d["residual"]) + mag) * 1.0001
+    assert np.all(np.abs(r - exact) <= bound)
+    # out is RMSNorm of the oracle's float32 residual_out, within one bf16 ulp
+    assert _close_bf16(o, _rmsnorm_bits(r, d["gamma"], d["eps"]))
+
+
+def test_finalize_k1_unit_weight_is_add_rmsnorm():
+    # k = 1, w = 1: fma(1, x, 0) = x, so residual_out = residual + x exactly (one float32
+    # add), and out is the textbook fused add + RMSNorm.
+    d = workloads.make_finalize_inputs(9, 520, E=4, k=1, seed=7, layout="random")
+    w = np.ones_like(d["weights"])
+    r, o = oracle.moe_finalize(d["expert_rows"], d["idx"], w, d["residual"], d["gamma"], d["eps"])
+    x = f32(d["expert_rows"])[d["idx"][:, 0]]
+    assert np.array_equal(r, d["residual"] + x)
+    assert _close_bf16(o, _rmsnorm_bits(r, d["gamma"], d["eps"]))
+
+
+def test_finalize_zero_weights_keep_residual():
+    d = workloads.make_finalize_inputs(6, 256, E=8, k=4, seed=8)
+    r, o = oracle.moe_finalize(d["expert_rows"], d["idx"], np.zeros_like(d["weights"]),
+                               d["residual"], d["gamma"], d["eps"])
+    assert np.array_equal(r, d["residual"])
+    assert _close_bf16(o, _rmsnorm_bits(d["residual"], d["gamma"], d["eps"]))
+
+
+def test_finalize_unit_gamma_rms_closed_form():
+    # gamma = 1: the RMS of r * (ms + eps)^-1/2 is sqrt(ms / (ms + eps)); bf16 rounding moves
+    # each element by at most 2^-9 relative.
+    d = workloads.make_finalize_inputs(8, 2048, E=16, k=4, seed=9)
+    gamma = workloads.to_bf16_bits(np.ones(2048, np.float32))
+    eps = 0.5  # large enough to show in the closed form
+    r, o = oracle.moe_finalize(d["expert_rows"], d["idx"], d["weights"], d["residual"], gamma, eps)
+    ms = (r.astype(np.float64) ** 2).mean(axis=1)
+    want = np.sqrt(ms / (ms + eps))
+    got = np.sqrt((f32(o).astype(np.float64) ** 2).mean(axis=1))
+    assert np.all(np.abs(got - want) <= 2.0 ** -9 * want)
+
+
+def test_finalize_integer_rows_exact():
+    # Small integers (exact in bf16), power-of-two weights and integer residuals keep every
+    # float32 step exact, so residual_out has a closed form; a wrong row, weight or a missing
+    # term shows up as a mismatch.
+    rng = np.random.default_rng(12)
+    T, H, k, n = 11, 72, 5, 11 * 5
+    rows = rng.integers(-8, 9, size=(n, H)).astype(np.float32)
+    idx = rng.permutation(n).astype(np.int32).reshape(T, k)
+    w = (2.0 ** rng.integers(-3, 2, size=(T, k))).astype(np.float32)
+    res = rng.integers(-50, 51, size=(T, H)).astype(np.float32)
+    gamma = workloads.to_bf16_bits(np.ones(H, np.float32))
+    r, _ = oracle.moe_finalize(workloads.to_bf16_bits(rows), idx, w, res, gamma, 1e-6)
+    want = res.astype(np.int64) * 8
+    for j in range(k):
+        want += (w[:, j:j + 1] * 8).astype(np.int64) * rows[idx[:, j]].astype(np.int64)
+    assert np.array_equal(r, (want / 8.0).astype(np.float32))
+
+
+def test_finalize_one_hot_weights_select_a_row():
+    d = workloads.make_finalize_inputs(10, 96, E=8, k=4, seed=13, layout="random")
+    rng = np.random.default_rng(14)
+    jstar = rng.integers(0, 4, size=10)
+    w = np.zeros_like(d["weights"])
+    w[np.arange(10), jstar] = 1.0
+    r, _ = oracle.moe_finalize(d["expert_rows"], d["idx"], w, np.zeros_like(d["residual"]),
+                               d["gamma"], d["eps"])
+    assert np.array_equal(r, f32(d["expert_rows"])[d["idx"][np.arange(10), jstar]])
+
+
+def test_finalize_permutation_equivariance():
+    d = workloads.make_finalize_inputs(12, 64, E=8, k=3, seed=15, layout="expert_sorted")
+    r0, o0 = oracle.moe_finalize(d["expert_rows"], d["idx"], d["weights"], d["residual"],
+                                 d["gamma"], d["eps"])
+    pi = np.random.default_rng(16).permutation(d["expert_rows"].shape[0])
+    rows = np.empty_like(d["expert_rows"])
+    rows[pi] = d["expert_rows"]            # row p moves to pi[p]
+    r1, o1 = oracle.moe_finalize(rows, pi[d["idx"]].astype(np.int32), d["weights"],
+                                 d["residual"], d["gamma"], d["eps"])
+    assert np.array_equal(r0, r1) and np.array_equal(o0, o1)
+
+
+def test_finalize_power_of_two_scaling():
+    # Scaling rows and residual by 2^m scales every float32 step exactly, and RMSNorm is
+    # scale invariant up to eps.
+    d = workloads.make_finalize_inputs(6, 128, E=8, k=4, seed=17)
+    r0, o0 = oracle.moe_finalize(d["expert_rows"], d["idx"], d["weights"], d["residual"],
+                                 d["gamma"], d["eps"])
+    rows4 = workloads.to_bf16_bits(f32(d["expert_rows"]) * 4)
+    r1, o1 = oracle.moe_finalize(rows4, d["idx"], d["weights"], d["residual"] * 4, d["gamma"],
+                                 d["eps"])
+    assert np.array_equal(r1, r0 * 4)
+    assert bf16_ulp_diff(o0, o1).max() <= 1
+
+
+def test_finalize_rejects_out_of_range_index():
+    d = workloads.make_finalize_inputs(2, 16, E=4, k=2, seed=18, layout="random")
+    bad = d["idx"].copy()
+    bad[1, 1] = d["expert_rows"].shape[0]
+    with pytest.raises(ValueError):
+        oracle.moe_finalize(d["expert_rows"], bad, d["weights"], d["residual"], d["gamma"], 1e-6)
+
+
+# ----------------------------------------------------------------------------- per-expert
+
+
+def _bf_per_expert(d):
+    x = f32(d["expert_rows"]).astype(np.float64)[d["idx"]]                 # [T,k,H]
+    scale = 1.0 / np.sqrt((x * x).mean(axis=2, keepdims=True) + d["eps"])
+    y = x * scale * f32(d["expert_gamma"]).astype(np.float64)[d["expert_ids"]]
+    terms = d["weights"][..., None].astype(np.float64) * y
+    return d["residual"].astype(np.float64) + terms.sum(axis=1), np.abs(terms).sum(axis=1)
+
+
+@pytest.mark.parametrize("T,H,k", [(1, 16, 1), (4, 96, 3), (16, 1024, 8)])
+def test_per_expert_brute_force(T, H, k):
+    d = workloads.make_finalize_inputs(T, H, E=16, k=k, seed=200 + T + k, per_expert=True,
+                                       residual_std=2.0)
+    r, o = oracle.moe_finalize(d["expert_rows"], d["idx"], d["weights"], d["residual"],
+                               d["gamma"], d["eps"], d["expert_ids"], d["expert_gamma"])
+    exact, mag = _bf_per_expert(d)
+    # one rounding of each normalised row to float32, k FMAs and the residual add
+    bound = (k + 2) * U32 * (np.abs(d["residual"]) + mag) * 1.0001
+    assert np.all(np.abs(r - exact) <= bound)
+    assert _close_bf16(o, _rmsnorm_bits(r, d["gamma"], d["eps"]))
+
+
+def test_per_expert_unit_gammas_ignore_expert_ids():
+    d = workloads.make_finalize_inputs(8, 64, E=16, k=4, seed=19, per_expert=True)
+    ones = workloads.to_bf16_bits(np.ones((16, 64), np.float32))
+    other = np.random.default_rng(20).integers(0, 16, size=d["expert_ids"].shape).astype(np.int32)
+    a = oracle.moe_finalize(d["expert_rows"], d["idx"], d["weights"], d["residual"], d["gamma"],
+                            d["eps"], d["expert_ids"], ones)
+    b = oracle.moe_finalize(d["expert_rows"], d["idx"], d["weights"], d["residual"], d["gamma"],
+                            d["eps"], other, ones)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_per_expert_single_row_closed_form():
+    # Every slot of a token reads the same row x through expert e, weights sum to 1, residual
+    # 0: residual_out = RMSNorm_e(x) = x / rms(x) * gammaE[e].
+    H, k = 256, 4
+    rng = np.random.default_rng(21)
+    x = workloads.to_bf16_bits(rng.standard_normal((1, H)).astype(np.float32))
+    ge = workloads.to_bf16_bits((1 + 0.1 * rng.standard_normal((3, H))).astype(np.float32))
+    idx = np.zeros((1, k), np.int32)
+    eids = np.full((1, k), 2, np.int32)
+    w = np.array([[0.5, 0.25, 0.125, 0.125]], np.float32)
+    r, _ = oracle.moe_finalize(x, idx, w, np.zeros((1, H), np.float32),
+                               workloads.to_bf16_bits(np.ones(H, np.float32)), 1e-6, eids, ge)
+    xv = f32(x[0]).astype(np.float64)
+    want = xv / np.sqrt((xv ** 2).mean() + 1e-6) * f32(ge[2]).astype(np.float64)
+    assert np.all(np.abs(r[0] - want) <= 3 * U32 * np.abs(want))
+
+
+def test_per_expert_row_scale_invariance():
+    # Each gathered row is normalised, so scaling every row by 2^m leaves residual_out
+    # unchanged up to the eps term.
+    d = workloads.make_finalize_inputs(5, 128, E=8, k=3, seed=22, per_expert=True)
+    a, _ = oracle.moe_finalize(d["expert_rows"], d["idx"], d["weights"], d["residual"],
+                               d["gamma"], 0.0, d["expert_ids"], d["expert_gamma"])
+    rows8 = workloads.to_bf16_bits(f32(d["expert_rows"]) * 8)
+    b, _ = oracle.moe_finalize(rows8, d["idx"], d["weights"], d["residual"], d["gamma"], 0.0,
+                               d["expert_ids"], d["expert_gamma"])
+    assert np.array_equal(a, b)  # with eps = 0 the scale cancels exactly
+
+
+# ----------------------------------------------------------------------------- gated
+
+
+def test_gated_brute_force_with_scipy_expit():
+    d = workloads.make_gated_inputs(7, 264, seed=23)
+    r, o = oracle.gated_residual_rmsnorm(d["x"], d["gate"], d["residual"], d["gamma"], d["eps"])
+    exact = d["residual"].astype(np.float64) + expit(f32(d["gate"]).astype(np.float64)) * \
+        f32(d["x"]).astype(np.float64)
+    # one rounding to float32 (half an ulp), plus a sliver for the float64 steps
+    assert np.all(np.abs(r - exact) <= 0.5001 * U32 * 2 * np.abs(exact) + 1e-30)
+    assert _close_bf16(o, _rmsnorm_bits(r, d["gamma"], d["eps"]))
+
+
+def test_gated_gate_zero_is_half():
+    # sigmoid(0) = 1/2 exactly, and x/2 is exact, so residual_out = float32 add.
+    d = workloads.make_gated_inputs(5, 128, seed=24)
+    zero = np.zeros_like(d["gate"])
+    r, _ = oracle.gated_residual_rmsnorm(d["x"], zero, d["residual"], d["gamma"], d["eps"])
+    assert np.array_equal(r, d["residual"] + np.float32(0.5) * f32(d["x"]))
+
+
+def test_gated_large_gate_is_add_rmsnorm():
+    d = workloads.make_gated_inputs(5, 512, seed=25)
+    g40 = workloads.to_bf16_bits(np.full(d["gate"].shape, 40.0, np.float32))
+    r, o = oracle.gated_residual_rmsnorm(d["x"], g40, d["residual"], d["gamma"], d["eps"])
+    plain = d["residual"] + f32(d["x"])
+    # sigmoid(40) = 1 - 4.2e-18: within one float32 ulp of the plain add
+    assert np.all(np.abs(r - plain) <= U32 * 2 * np.abs(plain))
+    assert _close_bf16(o, _rmsnorm_bits(plain, d["gamma"], d["eps"]))
+
+
+def test_gated_very_negative_gate_keeps_residual():
+    d = workloads.make_gated_inputs(4, 256, seed=26)
+    res = d["residual"].copy()
+    res[np.abs(res) < 1e-3] = 1e-3  # sigmoid(-30)*|x| < 4e-13 is below half an ulp here
+    gm30 = workloads.to_bf16_bits(np.full(d["gate"].shape, -30.0, np.float32))
+    r, _ = oracle.gated_residual_rmsnorm(d["x"], gm30, res, d["gamma"], d["eps"])
+    assert np.array_equal(r, res)
+
+
+# ----------------------------------------------------------------------------- per-head
+
+
+def _bf_per_head(d):
+    x = f32(d["x"]).astype(np.float64)
+    scale = 1.0 / np.sqrt((x * x).mean(axis=2, keepdims=True) + d["eps"])
+    return x * scale * f32(d["gamma"]).astype(np.float64) * expit(f32(d["gate"]).astype(np.float64))
+
+
+def test_per_head_brute_force():
+    d = workloads.make_per_head_inputs(5, 3, 64, seed=27)  # T, heads and D all differ
+    o = oracle.rmsnorm_sigmoid_gate(d["x"], d["gate"], d["gamma"], d["eps"])
+    assert _close_bf16(o, torch_bf16_bits(_bf_per_head(d)))
+
+
+def test_per_head_large_gate_is_rms_norm_over_head_dim():
+    d = workloads.make_per_head_inputs(6, 4, 64, seed=28)
+    g40 = workloads.to_bf16_bits(np.full(d["gate"].shape, 40.0, np.float32))
+    o = oracle.rmsnorm_sigmoid_gate(d["x"], g40, d["gamma"], d["eps"])
+    want = _rmsnorm_bits(f32(d["x"]).astype(np.float64), d["gamma"], d["eps"])
+    assert _close_bf16(o, want)
+
+
+def test_per_head_unit_gamma_rms_is_one():
+    d = workloads.make_per_head_inputs(4, 8, 64, seed=29)
+    ones = workloads.to_bf16_bits(np.ones(64, np.float32))
+    g40 = workloads.to_bf16_bits(np.full(d["gate"].shape, 40.0, np.float32))
+    o = oracle.rmsnorm_sigmoid_gate(d["x"], g40, ones, 0.0)
+    rms = np.sqrt((f32(o).astype(np.float64) ** 2).mean(axis=2))
+    assert np.all(np.abs(rms - 1.0) <= 2.0 ** -9)
+
+
+def test_per_head_heads_are_independent():
+    # Permuting the heads of x and gate permutes the output heads: the norm runs over D only.
+    d = workloads.make_per_head_inputs(3, 5, 64, seed=30)
+    o = oracle.rmsnorm_sigmoid_gate(d["x"], d["gate"], d["gamma"], d["eps"])
+    p = np.array([3, 0, 4, 1, 2])
+    o2 = oracle.rmsnorm_sigmoid_gate(d["x"][:, p], d["gate"][:, p], d["gamma"], d["eps"])
+    assert np.array_equal(o[:, p], o2)

@@ -1,0 +1,70 @@
+"""The seeded input generator: determinism and the structure of each workload (CPU only)."""
+import numpy as np
+import pytest
+
+import workloads
+from tests.helpers import f32
+
+
+def test_same_seed_same_bytes():
+    a = workloads.make_inputs("finalize_tiny")
+    b = workloads.make_inputs("finalize_tiny")
+    for key in ("expert_rows", "idx", "weights", "expert_ids", "residual", "gamma"):
+        assert np.array_equal(a[key], b[key]), key
+    c = workloads.make_inputs("finalize_tiny", seed=99)
+    assert not np.array_equal(a["expert_rows"], c["expert_rows"])
+
+
+@pytest.mark.parametrize("layout", ["random", "expert_sorted"])
+def test_idx_is_a_bijection(layout):
+    d = workloads.make_finalize_inputs(37, 16, E=12, k=5, seed=3, layout=layout)
+    assert d["idx"].dtype == np.int32 and d["idx"].shape == (37, 5)
+    assert np.array_equal(np.sort(d["idx"].ravel()), np.arange(37 * 5))
+
+
+def test_expert_sorted_rows_are_grouped_by_expert():
+    d = workloads.make_finalize_inputs(64, 16, E=32, k=8, seed=4, layout="expert_sorted")
+    n = 64 * 8
+    expert_of_row = np.empty(n, np.int64)
+    expert_of_row[d["idx"].ravel()] = d["expert_ids"].ravel()
+    assert np.all(np.diff(expert_of_row) >= 0)
+    # stable: within one expert, rows follow the flattened (t, j) slot order
+    slot_of_row = np.empty(n, np.int64)
+    slot_of_row[d["idx"].ravel()] = np.arange(n)
+    same = np.diff(expert_of_row) == 0
+    assert np.all(np.diff(slot_of_row)[same] > 0)
+
+
+def test_routing_weights_are_a_topk_softmax():
+    d = workloads.make_finalize_inputs(50, 8, E=16, k=4, seed=5)
+    w = d["weights"].astype(np.float64)
+    assert np.allclose(w.sum(axis=1), 1.0, atol=1e-6)
+    assert np.all(np.diff(w, axis=1) <= 0)          # descending logit order
+    for t in range(50):                              # distinct experts per token
+        assert len(set(d["expert_ids"][t])) == 4
+    assert d["expert_ids"].min() >= 0 and d["expert_ids"].max() < 16
+
+
+def test_topk_ties_go_to_lower_expert_id():
+    class Flat:  # a stand-in rng whose logits are all equal
+        @staticmethod
+        def standard_normal(shape):
+            return np.zeros(shape)
+    ids, w = workloads.topk_softmax_routing(Flat(), 3, 6, 2)
+    assert np.array_equal(ids, [[0, 1]] * 3) and np.allclose(w, 0.5)
+
+
+def test_shapes_and_dtypes_of_named_workloads():
+    d = workloads.make_inputs("finalize_decode_per_expert")
+    assert d["expert_rows"].shape == (64 * 8, 4096) and d["expert_rows"].dtype == np.uint16
+    assert d["expert_gamma"].shape == (128, 4096) and d["expert_gamma"].dtype == np.uint16
+    assert d["residual"].dtype == np.float32 and abs(d["residual"].std() - 2.0) < 0.05
+    g = workloads.make_inputs("gated_residual_rmsnorm", T=8)
+    assert g["x"].shape == (8, 8192) and abs(f32(g["gate"]).std() - 2.0) < 0.05
+    p = workloads.make_inputs("rmsnorm_sigmoid_gate", T=4)
+    assert p["x"].shape == (4, 64, 64) and p["gamma"].shape == (64,)
+
+
+def test_bf16_inputs_are_rounded_to_nearest_even():
+    v = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.5], np.float32)
+    assert list(workloads.to_bf16_bits(v)) == [0x3F80, 0x3F82, 0xC020]

@@ -1,0 +1,172 @@
+"""Seeded synthetic inputs for the MoE finalize path and its two sibling fused norms.
+
+This module only draws random inputs.  It holds none of the arithmetic the path computes:
+no gather, no accumulation, no normalisation and no output rounding.  The oracle, the GPU
+tests, ``bench.py`` and ``__graft_entry__.smoke()`` all take their inputs from here, so both
+sides of every parity check see the same bytes.
+
+Recipe (numpy ``default_rng(seed)``, PCG64; draws happen in the order listed):
+
+* MoE finalize (``make_finalize_inputs``):
+    1. routing logits ``[T, E]`` ~ N(0, 1) in float64;
+    2. the top-k experts per token: a stable argsort of the negated logits, so the k
+       largest logits come first, in descending order, and ties go to the lower expert id;
+    3. routing weights: a softmax over those k logits, in float64, cast to float32;
+    4. the unpermute index ``idx [T, k]`` (int32): the permuted GEMM2 output row that holds
+       the output of slot (t, j):
+         - ``layout="random"``: ``rng.permutation(T*k)``;
+         - ``layout="expert_sorted"``: a stable sort of the flattened (t, j) slots by expert
+           id, which is the contiguous grouped-GEMM layout (rows grouped by expert);
+    5. expert rows ``[T*k, H]`` ~ N(0, 1), drawn as float32 in chunks of 2**24 values and
+       rounded to bfloat16 (round-to-nearest-even, by torch's CPU cast);
+    6. residual ``[T, H]`` float32 ~ N(0, residual_std);
+    7. gamma ``[H]`` = 1 + 0.1 * N(0, 1), rounded to bfloat16;
+    8. (per-expert variant only) expert gammas ``[E, H]`` = 1 + 0.1 * N(0, 1), bfloat16.
+* Gated-residual RMSNorm (``make_gated_inputs``): x ``[T, H]`` ~ N(0, 1) bf16,
+  gate ``[T, H]`` ~ N(0, 2) bf16 (standard deviation 2), residual ``[T, H]`` ~ N(0, 1) fp32,
+  gamma ``[H]`` = 1 + 0.1 * N(0, 1) bf16.
+* Per-head RMSNorm + sigmoid gate (``make_per_head_inputs``): x ``[T, heads, D]`` ~ N(0, 1)
+  bf16, gate ``[T, heads, D]`` ~ N(0, 2) bf16, gamma ``[D]`` = 1 + 0.1 * N(0, 1) bf16.
+
+bfloat16 arrays are returned as ``numpy.uint16`` holding the raw bit patterns.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+CHUNK = 1 << 24  # values per draw when filling large arrays
+
+#: The five named workloads, with the sizes the MoE finalize pages and their model
+#: configurations work at.  ``seed`` fixes every draw.
+WORKLOADS = {
+    # Tiny finalize: correctness-sized, random permutation.
+    "finalize_tiny": dict(kind="finalize", T=16, H=1024, E=8, k=2, seed=1,
+                          layout="random", per_expert=False, residual_std=1.0),
+    # Decode-sized finalize with a per-expert RMSNorm on every gathered row
+    # (tensor-parallel finalize at hidden 4096, top-k 8).
+    "finalize_decode_per_expert": dict(kind="finalize", T=64, H=4096, E=128, k=8, seed=2,
+                                       layout="expert_sorted", per_expert=True,
+                                       residual_std=2.0),
+    # Prefill-sized deterministic finalize: the throughput workload.
+    "finalize_prefill": dict(kind="finalize", T=16384, H=7168, E=256, k=8, seed=3,
+                             layout="expert_sorted", per_expert=False, residual_std=1.0),
+    # Gated-residual RMSNorm at its fixed hidden size.
+    "gated_residual_rmsnorm": dict(kind="gated", T=4096, H=8192, seed=4),
+    # Per-head RMSNorm + sigmoid gate at its fixed head dim.
+    "rmsnorm_sigmoid_gate": dict(kind="per_head", T=4096, heads=64, D=64, seed=5),
+}
+
+EPS = 1e-6
+
+
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round a float32 array to bfloat16 (nearest, ties to even) and return the bit patterns."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _normal_f32(rng: np.random.Generator, n: int, std: float = 1.0) -> np.ndarray:
+    out = np.empty(n, dtype=np.float32)
+    for s in range(0, n, CHUNK):
+        e = min(n, s + CHUNK)
+        rng.standard_normal(out=out[s:e], dtype=np.float32)
+    if std != 1.0:
+        out *= np.float32(std)
+    return out
+
+
+def _normal_bf16(rng: np.random.Generator, n: int, std: float = 1.0) -> np.ndarray:
+    out = np.empty(n, dtype=np.uint16)
+    buf = np.empty(min(n, CHUNK), dtype=np.float32)
+    for s in range(0, n, CHUNK):
+        e = min(n, s + CHUNK)
+        b = buf[: e - s]
+        rng.standard_normal(out=b, dtype=np.float32)
+        if std != 1.0:
+            b *= np.float32(std)
+        out[s:e] = to_bf16_bits(b)
+    return out
+
+
+def topk_softmax_routing(rng: np.random.Generator, T: int, E: int, k: int):
+    """Top-k routing from N(0,1) logits: (expert_ids [T,k] int32, weights [T,k] float32).
+
+    Experts are listed by descending logit (ties to the lower id); the weights are a
+    softmax over the k selected logits.
+    """
+    if not 1 <= k <= E:
+        raise ValueError(f"need 1 <= k <= E, got k={k}, E={E}")
+    logits = rng.standard_normal((T, E))
+    order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+    top = np.take_along_axis(logits, order, axis=1)
+    z = np.exp(top - top[:, :1])
+    w = z / z.sum(axis=1, keepdims=True)
+    return order.astype(np.int32), w.astype(np.float32)
+
+
+def unpermute_index(rng: np.random.Generator, expert_ids: np.ndarray, layout: str) -> np.ndarray:
+    """idx[t, j] = the permuted row that holds slot (t, j)'s expert output."""
+    T, k = expert_ids.shape
+    n = T * k
+    if layout == "random":
+        return rng.permutation(n).astype(np.int32).reshape(T, k)
+    if layout == "expert_sorted":
+        # perm[p] = flattened slot stored at permuted row p (rows grouped by expert).
+        perm = np.argsort(expert_ids.ravel(), kind="stable")
+        idx = np.empty(n, dtype=np.int64)
+        idx[perm] = np.arange(n)
+        return idx.astype(np.int32).reshape(T, k)
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def make_finalize_inputs(T: int, H: int, E: int, k: int, seed: int, layout: str = "expert_sorted",
+                         per_expert: bool = False, residual_std: float = 1.0) -> dict:
+    rng = np.random.default_rng(seed)
+    expert_ids, w = topk_softmax_routing(rng, T, E, k)
+    idx = unpermute_index(rng, expert_ids, layout)
+    rows = _normal_bf16(rng, T * k * H).reshape(T * k, H)
+    residual = _normal_f32(rng, T * H, residual_std).reshape(T, H)
+    gamma = to_bf16_bits(1.0 + 0.1 * _normal_f32(rng, H))
+    d = dict(kind="finalize", T=T, H=H, E=E, k=k, eps=EPS, expert_rows=rows, idx=idx,
+             weights=w, expert_ids=expert_ids, residual=residual, gamma=gamma,
+             expert_gamma=None)
+    if per_expert:
+        d["expert_gamma"] = to_bf16_bits(1.0 + 0.1 * _normal_f32(rng, E * H)).reshape(E, H)
+    return d
+
+
+def make_gated_inputs(T: int, H: int, seed: int) -> dict:
+    rng = np.random.default_rng(seed)
+    x = _normal_bf16(rng, T * H).reshape(T, H)
+    gate = _normal_bf16(rng, T * H, 2.0).reshape(T, H)
+    residual = _normal_f32(rng, T * H).reshape(T, H)
+    gamma = to_bf16_bits(1.0 + 0.1 * _normal_f32(rng, H))
+    return dict(kind="gated", T=T, H=H, eps=EPS, x=x, gate=gate, residual=residual, gamma=gamma)
+
+
+def make_per_head_inputs(T: int, heads: int, D: int, seed: int) -> dict:
+    rng = np.random.default_rng(seed)
+    x = _normal_bf16(rng, T * heads * D).reshape(T, heads, D)
+    gate = _normal_bf16(rng, T * heads * D, 2.0).reshape(T, heads, D)
+    gamma = to_bf16_bits(1.0 + 0.1 * _normal_f32(rng, D))
+    return dict(kind="per_head", T=T, heads=heads, D=D, eps=EPS, x=x, gate=gate, gamma=gamma)
+
+
+def make_inputs(name: str, **overrides) -> dict:
+    """Inputs of a named workload; keyword overrides change its sizes or seed."""
+    cfg = dict(WORKLOADS[name])
+    cfg.update(overrides)
+    kind = cfg.pop("kind")
+    if kind == "finalize":
+        return make_finalize_inputs(**cfg)
+    if kind == "gated":
+        return make_gated_inputs(**cfg)
+    if kind == "per_head":
+        return make_per_head_inputs(**cfg)
+    raise ValueError(kind)
