@@ -1,0 +1,208 @@
+"""Python binding of libmf.so: the MI355X (gfx950) MoE finalize and its two sibling fused norms.
+
+The functions carry the names of the C entry points in include/mf.h and do argument
+marshalling only: they take torch tensors (device memory), optionally allocate the outputs
+with torch, and pass raw pointers, sizes and the current HIP stream to the library.  Every
+step of the computation runs in the library's HIP kernels.  There is no fallback: if the
+library is not built, or a tensor is not on the GPU, the call raises.
+
+bf16 tensors are torch.bfloat16; fp32 tensors torch.float32; indices torch.int32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MFError", "lib", "mf_moe_finalize", "mf_gated_residual_rmsnorm", "mf_rmsnorm_sigmoid_gate",
+    "mf_moe_finalize_supported", "mf_gated_residual_rmsnorm_supported",
+    "mf_rmsnorm_sigmoid_gate_supported", "mf_launch_shape", "mf_stream_copy", "mf_status_string",
+    "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmf.so")
+
+MF_OK = 0
+_lib = None
+
+
+class MFError(RuntimeError):
+    """A negative mf_status returned by the library."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {mf_status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmf.so (argument types set).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m finalize_residual_rmsnorm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, i32, f32, ci = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                                ctypes.c_int)
+        sig = {
+            "mf_moe_finalize": [p, i64, p, p, p, p, i32, p, p, p, f32, p, i64, i32, i32, p],
+            "mf_gated_residual_rmsnorm": [p, p, p, p, p, f32, p, i64, i32, p],
+            "mf_rmsnorm_sigmoid_gate": [p, p, p, f32, p, i64, i32, i32, p],
+            "mf_moe_finalize_supported": [i32, i32, ci],
+            "mf_gated_residual_rmsnorm_supported": [i32],
+            "mf_rmsnorm_sigmoid_gate_supported": [i32],
+            "mf_launch_shape": [ci, i64, i32, i32, p, p, p, p],
+            "mf_stream_copy": [p, p, i64, p],
+            "mf_status_string": [ci],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.mf_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def mf_status_string(status: int) -> str:
+    return lib().mf_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MF_OK:
+        raise MFError(fn, status)
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor, got device {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+
+
+def mf_moe_finalize(expert_rows: torch.Tensor, idx: torch.Tensor, weights: torch.Tensor,
+                    residual: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, *,
+                    expert_ids: torch.Tensor | None = None,
+                    expert_gamma: torch.Tensor | None = None,
+                    residual_out: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                    stream=None):
+    """MoE finalize + residual add + RMSNorm.  Returns (out bf16 [T,H], residual_out fp32 [T,H]).
+
+    expert_rows bf16 [num_rows, H]; idx int32 [T, k]; weights fp32 [T, k]; residual fp32 [T, H];
+    gamma bf16 [H]; optional expert_ids int32 [T, k] + expert_gamma bf16 [E, H] for the
+    per-expert RMSNorm variant.  Pass residual_out=residual to update the residual in place.
+    """
+    T, k = idx.shape
+    num_rows, H = expert_rows.shape
+    dev = expert_rows.device
+    if residual_out is None:
+        residual_out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    pe = pg = None
+    E = 0
+    if (expert_ids is None) != (expert_gamma is None):
+        raise ValueError("expert_ids and expert_gamma go together")
+    if expert_gamma is not None:
+        E = expert_gamma.shape[0]
+        pe = _dev(expert_ids, torch.int32, "expert_ids", (T, k))
+        pg = _dev(expert_gamma, torch.bfloat16, "expert_gamma", (E, H))
+    st = lib().mf_moe_finalize(
+        _dev(expert_rows, torch.bfloat16, "expert_rows"), num_rows,
+        _dev(idx, torch.int32, "idx"), _dev(weights, torch.float32, "weights", (T, k)), pe, pg, E,
+        _dev(residual, torch.float32, "residual", (T, H)),
+        _dev(residual_out, torch.float32, "residual_out", (T, H)),
+        _dev(gamma, torch.bfloat16, "gamma", (H,)), float(eps),
+        _dev(out, torch.bfloat16, "out", (T, H)), T, H, k, _stream(stream, dev))
+    _check("mf_moe_finalize", st)
+    return out, residual_out
+
+
+def mf_gated_residual_rmsnorm(x: torch.Tensor, gate: torch.Tensor, residual: torch.Tensor,
+                              gamma: torch.Tensor, eps: float = 1e-6, *,
+                              residual_out: torch.Tensor | None = None,
+                              out: torch.Tensor | None = None, stream=None):
+    """Gated-residual RMSNorm.  Returns (out bf16 [T,H], residual_out fp32 [T,H])."""
+    T, H = x.shape
+    dev = x.device
+    if residual_out is None:
+        residual_out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    st = lib().mf_gated_residual_rmsnorm(
+        _dev(x, torch.bfloat16, "x"), _dev(gate, torch.bfloat16, "gate", (T, H)),
+        _dev(residual, torch.float32, "residual", (T, H)),
+        _dev(residual_out, torch.float32, "residual_out", (T, H)),
+        _dev(gamma, torch.bfloat16, "gamma", (H,)), float(eps),
+        _dev(out, torch.bfloat16, "out", (T, H)), T, H, _stream(stream, dev))
+    _check("mf_gated_residual_rmsnorm", st)
+    return out, residual_out
+
+
+def mf_rmsnorm_sigmoid_gate(x: torch.Tensor, gate: torch.Tensor, gamma: torch.Tensor,
+                            eps: float = 1e-6, *, out: torch.Tensor | None = None, stream=None):
+    """Per-head RMSNorm + sigmoid gate over x [T, heads, head_dim].  Returns out (bf16)."""
+    T, heads, D = x.shape
+    dev = x.device
+    if out is None:
+        out = torch.empty_like(x)
+    st = lib().mf_rmsnorm_sigmoid_gate(
+        _dev(x, torch.bfloat16, "x"), _dev(gate, torch.bfloat16, "gate", (T, heads, D)),
+        _dev(gamma, torch.bfloat16, "gamma", (D,)), float(eps),
+        _dev(out, torch.bfloat16, "out", (T, heads, D)), T, heads, D, _stream(stream, dev))
+    _check("mf_rmsnorm_sigmoid_gate", st)
+    return out
+
+
+def mf_moe_finalize_supported(H: int, k: int, per_expert: bool = False) -> bool:
+    return bool(lib().mf_moe_finalize_supported(H, k, int(per_expert)))
+
+
+def mf_gated_residual_rmsnorm_supported(H: int) -> bool:
+    return bool(lib().mf_gated_residual_rmsnorm_supported(H))
+
+
+def mf_rmsnorm_sigmoid_gate_supported(head_dim: int) -> bool:
+    return bool(lib().mf_rmsnorm_sigmoid_gate_supported(head_dim))
+
+
+KIND_FINALIZE, KIND_FINALIZE_PER_EXPERT, KIND_GATED = 0, 1, 2
+
+
+def mf_launch_shape(kind: int, T: int, H: int, k: int = 1) -> dict:
+    """The launch shape the library picks: waves per token, vectors per lane, block, grid."""
+    wpt, vpl, blk = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    grid = ctypes.c_int64()
+    _check("mf_launch_shape", lib().mf_launch_shape(kind, T, H, k, ctypes.byref(wpt),
+                                                    ctypes.byref(vpl), ctypes.byref(blk),
+                                                    ctypes.byref(grid)))
+    return dict(waves_per_token=wpt.value, vectors_per_lane=vpl.value, block=blk.value,
+                grid=grid.value)
+
+
+def mf_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Copy src into dst (same byte size, a multiple of 16) with the library's copy kernel."""
+    if src.device.type != "cuda" or dst.device.type != "cuda":
+        raise ValueError("mf_stream_copy: GPU tensors required")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("mf_stream_copy: contiguous tensors required")
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("mf_stream_copy: size mismatch")
+    _check("mf_stream_copy", lib().mf_stream_copy(src.data_ptr(), dst.data_ptr(), n,
+                                                  _stream(stream, src.device)))

@@ -1,0 +1,163 @@
+// The two fused norms that sit beside the MoE finalize, and a streaming copy used to
+// measure the achievable HBM bandwidth.
+#pragma once
+
+#include "row_norm.h"
+
+namespace mf {
+
+// ---------------------------------------------------------------------------------------
+// Gated-residual RMSNorm (page "FlashInfer: fused norms and TP/EP MoE for Muse-Spark-Open",
+// PR #6544, section 1.1, and its "Fixed-Width Fused Norms" docs at hidden size 8192):
+//   residual_out = residual + sigmoid(gate) * x      (fp32 stream, one rounding via fma)
+//   out = bf16(residual_out * (mean(residual_out^2) + eps)^-1/2 * gamma)
+// Same row mapping and fixed reduction tree as the finalize kernel.  The sigmoid uses the
+// hardware exp2 and an IEEE division so that residual_out stays within a few fp32 ulps of
+// the exact value; that keeps the kernel bound by HBM rather than by the transcendental.
+struct GatedArgs {
+    const uint16_t* x;       // bf16 [T, H]
+    const uint16_t* gate;    // bf16 [T, H]
+    const float* residual;   // [T, H]
+    float* residual_out;     // [T, H], may equal residual
+    const uint16_t* gamma;   // bf16 [H]
+    uint16_t* out;           // bf16 [T, H]
+    int64_t T;
+    int32_t H;
+    int32_t wpt;
+    int32_t spw;
+    float eps;
+};
+
+__device__ __forceinline__ float sigmoid_accurate(float g) {
+    return 1.0f / (1.0f + __expf(-g));
+}
+
+template <int VPL>
+__global__ void __launch_bounds__(block_max_for(VPL))
+gated_residual_rmsnorm_kernel(const GatedArgs a) {
+    extern __shared__ float lds[];
+    const RowMap m = row_map(a.T, a.wpt);
+    if (a.wpt == 1 && !m.valid) return;
+
+    const int H = a.H;
+    int eoff[VPL];
+    bool sval[VPL];
+#pragma unroll
+    for (int s = 0; s < VPL; ++s) {
+        const int e = (m.wit * a.spw + s) * kSlot + m.lane * kVec;
+        sval[s] = e < H;
+        eoff[s] = sval[s] ? e : 0;
+    }
+    const int64_t row = m.t * H;
+    const uint16_t* xr = a.x + row;
+    const uint16_t* gr = a.gate + row;
+    const float* res = a.residual + row;
+
+    float r[VPL][8];
+#pragma unroll
+    for (int s = 0; s < VPL; ++s) {
+        const u32x4 xv = ld_stream(reinterpret_cast<const u32x4*>(xr + eoff[s]));
+        const u32x4 gv = ld_stream(reinterpret_cast<const u32x4*>(gr + eoff[s]));
+        const f32x4 r0 = ld_stream(reinterpret_cast<const f32x4*>(res + eoff[s]));
+        const f32x4 r1 = ld_stream(reinterpret_cast<const f32x4*>(res + eoff[s] + 4));
+        float x[8], g[8];
+        widen8(xv, x);
+        widen8(gv, g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            r[s][i] = __builtin_fmaf(sigmoid_accurate(g[i]), x[i], r0[i]);
+            r[s][4 + i] = __builtin_fmaf(sigmoid_accurate(g[4 + i]), x[4 + i], r1[i]);
+        }
+    }
+    float* res_out = a.residual_out + row;
+    if (m.valid) {
+#pragma unroll
+        for (int s = 0; s < VPL; ++s) {
+            if (sval[s]) {
+                st_stream(f32x4{r[s][0], r[s][1], r[s][2], r[s][3]},
+                          reinterpret_cast<f32x4*>(res_out + eoff[s]));
+                st_stream(f32x4{r[s][4], r[s][5], r[s][6], r[s][7]},
+                          reinterpret_cast<f32x4*>(res_out + eoff[s] + 4));
+            }
+        }
+    }
+    int parity = 0;
+    rmsnorm_store<VPL>(r, eoff, sval, a.gamma, a.out + row, H, a.eps, lds, parity, m);
+}
+
+// ---------------------------------------------------------------------------------------
+// Per-head RMSNorm with a sigmoid gate (PR #6544 page, section 1.2; head dim 64):
+//   out[t,n,:] = bf16(((x * (mean(x^2) + eps)^-1/2) * gamma) * sigmoid(gate))
+// One head is 64 bf16 = 128 bytes = 8 lanes x 16 bytes, so a wave covers 8 heads per
+// instruction; the sum of squares is reduced in fp32 across the 8 lanes of the head with
+// DPP.  Each wave handles GPW groups of 8 heads, all loads issued before use.  The output is
+// bf16, so a hardware reciprocal is ample for the sigmoid here.
+struct PerHeadArgs {
+    const uint16_t* x;      // bf16 [T*heads, 64]
+    const uint16_t* gate;   // bf16 [T*heads, 64]
+    const uint16_t* gamma;  // bf16 [64]
+    uint16_t* out;          // bf16 [T*heads, 64]
+    int64_t num_heads_total;
+    float eps;
+};
+
+constexpr int kHeadDim = 64;
+constexpr int kHeadsPerWaveLoad = kWave * kVec / kHeadDim;  // 8
+
+template <int GPW>
+__global__ void __launch_bounds__(256) rmsnorm_sigmoid_gate_kernel(const PerHeadArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int d0 = (lane & 7) * kVec;
+    const int64_t last = a.num_heads_total - 1;
+
+    float gm[8];
+    widen8(*reinterpret_cast<const u32x4*>(a.gamma + d0), gm);
+
+    u32x4 xv[GPW], gv[GPW];
+    int64_t head[GPW];
+#pragma unroll
+    for (int g = 0; g < GPW; ++g) {
+        head[g] = (wave * GPW + g) * kHeadsPerWaveLoad + (lane >> 3);
+        const int64_t hc = head[g] < last ? head[g] : last;
+        xv[g] = ld_stream(reinterpret_cast<const u32x4*>(a.x + hc * kHeadDim + d0));
+        gv[g] = ld_stream(reinterpret_cast<const u32x4*>(a.gate + hc * kHeadDim + d0));
+    }
+#pragma unroll
+    for (int g = 0; g < GPW; ++g) {
+        float x[8], gt[8];
+        widen8(xv[g], x);
+        widen8(gv[g], gt);
+        const float ss = sum8_lanes(sumsq8(x));
+        const float inv = 1.0f / __builtin_sqrtf(ss * (1.0f / kHeadDim) + a.eps);
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float s0 = __builtin_amdgcn_rcpf(1.0f + __expf(-gt[2 * i]));
+            const float s1 = __builtin_amdgcn_rcpf(1.0f + __expf(-gt[2 * i + 1]));
+            o[i] = pack_bf16x2(((x[2 * i] * inv) * gm[2 * i]) * s0,
+                               ((x[2 * i + 1] * inv) * gm[2 * i + 1]) * s1);
+        }
+        if (head[g] <= last) st_stream(o, reinterpret_cast<u32x4*>(a.out + head[g] * kHeadDim + d0));
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Streaming copy with 16-byte vectors, U vectors in flight per lane.
+template <int U>
+__global__ void __launch_bounds__(256) stream_copy_kernel(const u32x4* src, u32x4* dst, int64_t n) {
+    const int64_t base = (int64_t)blockIdx.x * (blockDim.x * U) + threadIdx.x;
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t i = base + (int64_t)u * blockDim.x;
+        if (i < n) v[u] = ld_stream(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t i = base + (int64_t)u * blockDim.x;
+        if (i < n) st_stream(v[u], dst + i);
+    }
+}
+
+}  // namespace mf

@@ -1,0 +1,137 @@
+/*
+ * mf.h - C ABI of the MI355X (gfx950) MoE finalize library and its two sibling fused norms.
+ *
+ * Sources of the operations (pages on FlashInfer pull requests; section names as on each page):
+ *  [PR5319] "FlashInfer MoE performance: improving the deterministic finalize with CuTe DSL",
+ *           section 1 (the new CuTe DSL finalize kernel and its _fma_rn helper).
+ *  [PR6544] "FlashInfer: fused norms and TP/EP MoE for Muse-Spark-Open", sections 1.1
+ *           (gated residual RMSNorm), 1.2 (RMSNorm + sigmoid gate), 2.1 (TP MoE finalize),
+ *           2.4 (MoE finalize + RMSNorm + all-reduce) and the "Fixed-Width Fused Norms" docs.
+ *  [PR4730] "MoE all-reduce fusion for Blackwell: FlashInfer's Cake backend", section 2
+ *           (fusion strategy: expert sum, residual add and RMSNorm in one launch).
+ *
+ * Conventions for every entry point:
+ *  - Tensors are dense and row-major.  bfloat16 data is passed as raw 16-bit patterns
+ *    (uint16_t).  All tensor pointers are device pointers on the current HIP device.
+ *  - The caller owns every buffer.  The library allocates nothing, keeps no state between
+ *    calls and is safe to call from several threads.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the null stream).
+ *    The library never synchronizes.
+ *  - Arguments are checked on the host before any HIP call.  On a failed check the function
+ *    returns a negative mf_status and launches nothing.  A zero token count returns MF_OK
+ *    without a launch.
+ *  - Row pointers (bf16 and fp32 tensors with H or head_dim columns) must be 16-byte
+ *    aligned; idx, weights and expert_ids 4-byte aligned.
+ *  - Results are deterministic: the same inputs give bit-identical outputs, whatever the
+ *    token count, the stream or the launch shape chosen for it.
+ *  - Preconditions that are not checked (the kernels stay memory-safe if they are broken,
+ *    but the affected outputs are unspecified): indices lie in range, pointers are device
+ *    memory of the stated size.
+ */
+#ifndef MF_H
+#define MF_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mf_status {
+    MF_OK = 0,
+    MF_ERR_NULL = -1,        /* a required pointer is NULL */
+    MF_ERR_SHAPE = -2,       /* a size is negative or inconsistent */
+    MF_ERR_UNSUPPORTED = -3, /* a width or top-k outside what the *_supported queries accept */
+    MF_ERR_ALIGN = -4,       /* a pointer is not aligned as stated above */
+    MF_ERR_ALIAS = -5,       /* an output overlaps an input (except residual_out == residual) */
+    MF_ERR_VALUE = -6,       /* eps is negative, NaN or infinite */
+    MF_ERR_HIP = -7          /* the HIP runtime reported an error for the launch */
+} mf_status;
+
+/*
+ * MoE finalize fused with the residual add and RMSNorm ([PR5319] section 1; [PR6544]
+ * sections 2.1 and 2.4; [PR4730] section 2).
+ *
+ * For every token t in [0, T):
+ *   acc = +0 (fp32, H values)
+ *   for j = 0 .. k-1, in this order:
+ *       x = widen(expert_rows[idx[t,j], :])                               (bf16 -> fp32, exact)
+ *       if per-expert: x = x * (mean(x^2) + eps)^-1/2 * expert_gamma[expert_ids[t,j], :]
+ *       acc = fma(weights[t,j], x, acc)                      (fp32 fused multiply-add, RNE)
+ *   residual_out[t,:] = residual[t,:] + acc                                         (fp32)
+ *   out[t,:] = bf16_rne(residual_out[t,:] * (mean(residual_out[t,:]^2) + eps)^-1/2 * gamma)
+ *
+ *  expert_rows   bf16 [num_rows, H]: the permuted GEMM2 (FC2) output, one row per (t, j).
+ *  idx           int32 [T, k]: the row of expert_rows holding slot (t, j).  A gather: rows
+ *                may be in any order (e.g. grouped by expert); each is read where it lies.
+ *  weights       fp32 [T, k]: routing weights.
+ *  expert_ids    int32 [T, k] and expert_gamma bf16 [num_experts, H]: both NULL for the plain
+ *                finalize; both set for the per-expert-RMSNorm variant ([PR6544] 2.1).
+ *  residual      fp32 [T, H] in; residual_out fp32 [T, H] out.  residual_out may equal
+ *                residual (in-place update of the residual stream); partial overlap is
+ *                rejected.
+ *  gamma         bf16 [H]; eps >= 0; out bf16 [T, H].
+ * Supported: H % 8 == 0 and 8 <= H <= 131072; 1 <= k <= 64 (k <= 16 with the per-expert
+ * variant).  Out-of-range idx or expert_ids are clamped into range (memory-safe, result
+ * unspecified for that token).
+ */
+int mf_moe_finalize(const uint16_t* expert_rows, int64_t num_rows, const int32_t* idx,
+                    const float* weights, const int32_t* expert_ids,
+                    const uint16_t* expert_gamma, int32_t num_experts, const float* residual,
+                    float* residual_out, const uint16_t* gamma, float eps, uint16_t* out,
+                    int64_t T, int32_t H, int32_t k, void* stream);
+
+/*
+ * Gated-residual RMSNorm ([PR6544] section 1.1; fixed hidden size 8192 there, any
+ * supported H here):
+ *   residual_out = residual + sigmoid(gate) * x                 (fp32, sigmoid = 1/(1+e^-g))
+ *   out = bf16_rne(residual_out * (mean(residual_out^2) + eps)^-1/2 * gamma)
+ *  x, gate bf16 [T, H]; residual, residual_out fp32 [T, H] (may be equal); gamma bf16 [H];
+ *  out bf16 [T, H].  Supported: H % 8 == 0 and 8 <= H <= 131072.
+ */
+int mf_gated_residual_rmsnorm(const uint16_t* x, const uint16_t* gate, const float* residual,
+                              float* residual_out, const uint16_t* gamma, float eps,
+                              uint16_t* out, int64_t T, int32_t H, void* stream);
+
+/*
+ * Per-head RMSNorm with a sigmoid gate ([PR6544] section 1.2; head dim 64):
+ *   out[t,n,:] = bf16_rne(x[t,n,:] * (mean(x[t,n,:]^2) + eps)^-1/2 * gamma * sigmoid(gate[t,n,:]))
+ *  x, gate, out bf16 [T, num_heads, head_dim]; gamma bf16 [head_dim], shared by all heads.
+ *  The sum of squares is reduced in fp32.  Supported: head_dim == 64, num_heads >= 1.
+ */
+int mf_rmsnorm_sigmoid_gate(const uint16_t* x, const uint16_t* gate, const uint16_t* gamma,
+                            float eps, uint16_t* out, int64_t T, int32_t num_heads,
+                            int32_t head_dim, void* stream);
+
+/*
+ * Capability queries (the fixed-width contract of [PR6544]'s "Fixed-Width Fused Norms":
+ * check before calling and fall back otherwise).  Return 1 if supported, else 0.
+ */
+int mf_moe_finalize_supported(int32_t H, int32_t k, int per_expert);
+int mf_gated_residual_rmsnorm_supported(int32_t H);
+int mf_rmsnorm_sigmoid_gate_supported(int32_t head_dim);
+
+/*
+ * Launch shape that mf_moe_finalize / mf_gated_residual_rmsnorm use for a problem size:
+ * waves per token row, 16-byte vectors per lane (the row slice each lane holds), workgroup
+ * size and grid size.  Any output pointer may be NULL.  Returns MF_OK or MF_ERR_UNSUPPORTED.
+ * (kind: 0 = finalize, 1 = finalize with per-expert RMSNorm, 2 = gated-residual RMSNorm.)
+ */
+int mf_launch_shape(int kind, int64_t T, int32_t H, int32_t k, int32_t* waves_per_token,
+                    int32_t* vectors_per_lane, int32_t* block_threads, int64_t* grid_blocks);
+
+/*
+ * Streaming copy of `bytes` bytes (a multiple of 16; both pointers 16-byte aligned) with the
+ * same 16-byte vector loads and stores as the kernels above.  A measurement aid: it gives
+ * the achievable HBM copy bandwidth and calibrates the HBM byte counters.
+ */
+int mf_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+/* Human-readable name of a status code (never NULL). */
+const char* mf_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MF_H */

@@ -1,0 +1,156 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments with the documented status before any HIP call.
+No call here reaches a kernel launch (there is no GPU in this container)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import finalize_residual_rmsnorm_amd as mf
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mf.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, VALUE, HIP = 0, -1, -2, -3, -4, -5, -6, -7
+
+# Fake device addresses: never dereferenced, every call below fails validation first.
+A = 0x7F0000000000
+B = 0x7F0100000000
+C = 0x7F0200000000
+D = 0x7F0300000000
+E_ = 0x7F0400000000
+F = 0x7F0500000000
+G = 0x7F0600000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^(?:int|const char\*)\s+(mf_\w+)\(", text, flags=re.M)
+
+
+def test_header_symbols_are_exported():
+    names = declared_functions()
+    assert len(names) == 9, names
+    L = ctypes.CDLL(mf.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_cover_every_code():
+    for code in (OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, VALUE, HIP):
+        s = mf.mf_status_string(code)
+        assert s.startswith("MF_"), (code, s)
+    assert mf.mf_status_string(12345) == "unknown mf_status"
+
+
+def test_supported_queries():
+    assert mf.mf_moe_finalize_supported(7168, 8)
+    assert mf.mf_moe_finalize_supported(4096, 8, per_expert=True)
+    assert not mf.mf_moe_finalize_supported(7170, 8)       # H % 8 != 0
+    assert not mf.mf_moe_finalize_supported(32776, 8)      # beyond the widest row
+    assert not mf.mf_moe_finalize_supported(1024, 0)
+    assert not mf.mf_moe_finalize_supported(1024, 65)
+    assert mf.mf_gated_residual_rmsnorm_supported(8192)
+    assert not mf.mf_gated_residual_rmsnorm_supported(8190)
+    assert mf.mf_rmsnorm_sigmoid_gate_supported(64)
+    assert not mf.mf_rmsnorm_sigmoid_gate_supported(128)
+
+
+def fin(rows=A, num_rows=32, idx=B, w=C, eids=None, eg=None, E=0, res=D, res_out=E_,
+        gamma=F, eps=1e-6, out=G, T=16, H=1024, k=2):
+    return mf.lib().mf_moe_finalize(rows, num_rows, idx, w, eids, eg, E, res, res_out, gamma,
+                                    eps, out, T, H, k, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), SHAPE), (dict(num_rows=-1), SHAPE), (dict(H=1030), UNSUP), (dict(H=0), UNSUP),
+    (dict(k=0), UNSUP), (dict(k=65), UNSUP), (dict(rows=None), NULL), (dict(idx=None), NULL),
+    (dict(w=None), NULL), (dict(res=None), NULL), (dict(res_out=None), NULL),
+    (dict(gamma=None), NULL), (dict(out=None), NULL), (dict(eids=B + 4096), NULL),
+    (dict(eg=A + 8192), NULL), (dict(eids=B + 4096, eg=A + 1 << 20, E=0), SHAPE),
+    (dict(num_rows=0), SHAPE), (dict(eps=float("nan")), VALUE), (dict(eps=-1e-6), VALUE),
+    (dict(eps=float("inf")), VALUE), (dict(rows=A + 8), ALIGN), (dict(res_out=E_ + 4), ALIGN),
+    (dict(out=G + 2), ALIGN), (dict(idx=B + 2), ALIGN), (dict(gamma=F + 8), ALIGN),
+    (dict(res_out=D + 64), ALIAS), (dict(out=A + 1024), ALIAS), (dict(out=E_ + 4096), ALIAS),
+    (dict(res_out=B), ALIAS), (dict(out=F), ALIAS),
+    (dict(T=1 << 27), SHAPE),  # 64 lanes per token would overflow the 32-bit grid
+])
+def test_finalize_rejects_bad_arguments(kw, code):
+    assert fin(**kw) == code
+
+
+def test_finalize_zero_tokens_is_a_no_op():
+    assert fin(T=0, rows=None, idx=None, w=None, res=None, res_out=None, gamma=None,
+               out=None) == OK
+    assert fin(T=0, H=1001) == UNSUP  # widths are still checked
+
+
+def test_in_place_residual_passes_validation_up_to_launch():
+    # residual_out == residual is legal; stop just short of a launch with an unsupported
+    # width at T = 0 to show the alias check itself does not reject it.
+    assert fin(T=0, res_out=D) == OK
+
+
+def gated(x=A, gate=B, res=C, res_out=D, gamma=E_, eps=1e-6, out=F, T=8, H=8192):
+    return mf.lib().mf_gated_residual_rmsnorm(x, gate, res, res_out, gamma, eps, out, T, H, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), SHAPE), (dict(H=8196), UNSUP), (dict(x=None), NULL), (dict(gate=None), NULL),
+    (dict(res=None), NULL), (dict(res_out=None), NULL), (dict(gamma=None), NULL),
+    (dict(out=None), NULL), (dict(eps=float("nan")), VALUE), (dict(x=A + 2), ALIGN),
+    (dict(res_out=C + 16), ALIAS), (dict(out=A), ALIAS), (dict(out=D + 32), ALIAS),
+])
+def test_gated_rejects_bad_arguments(kw, code):
+    assert gated(**kw) == code
+    assert gated(T=0) == OK
+
+
+def per_head(x=A, gate=B, gamma=C, eps=1e-6, out=D, T=4, heads=64, dim=64):
+    return mf.lib().mf_rmsnorm_sigmoid_gate(x, gate, gamma, eps, out, T, heads, dim, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), SHAPE), (dict(heads=0), SHAPE), (dict(dim=128), UNSUP), (dict(x=None), NULL),
+    (dict(gate=None), NULL), (dict(gamma=None), NULL), (dict(out=None), NULL),
+    (dict(eps=-1.0), VALUE), (dict(out=D + 8), ALIGN), (dict(out=A + 256), ALIAS),
+])
+def test_per_head_rejects_bad_arguments(kw, code):
+    assert per_head(**kw) == code
+    assert per_head(T=0) == OK
+
+
+def test_stream_copy_rejects_bad_arguments():
+    L = mf.lib()
+    assert L.mf_stream_copy(A, B, -16, None) == SHAPE
+    assert L.mf_stream_copy(A, B, 24, None) == SHAPE
+    assert L.mf_stream_copy(A, B, 0, None) == OK
+    assert L.mf_stream_copy(None, B, 16, None) == NULL
+    assert L.mf_stream_copy(A + 8, B, 16, None) == ALIGN
+    assert L.mf_stream_copy(A, A + 16, 64, None) == ALIAS
+
+
+def test_launch_shapes():
+    # prefill: a wave per token row, 14 slots of 512 values per lane, 4 tokens per workgroup
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 16384, 7168, 8) == dict(
+        waves_per_token=1, vectors_per_lane=14, block=256, grid=4096)
+    # decode with per-expert norm: the row is spread over 8 waves
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE_PER_EXPERT, 64, 4096, 8) == dict(
+        waves_per_token=8, vectors_per_lane=1, block=512, grid=64)
+    # tiny: H = 1024 is two slots, one per wave
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 16, 1024, 2) == dict(
+        waves_per_token=2, vectors_per_lane=1, block=256, grid=8)
+    assert mf.mf_launch_shape(mf.KIND_GATED, 4096, 8192)["vectors_per_lane"] == 16
+    # the widest row needs 4 waves of 16 slots
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 100000, 32768, 8)["waves_per_token"] == 4
+    with pytest.raises(mf.MFError):
+        mf.mf_launch_shape(mf.KIND_FINALIZE, 4, 1001, 2)
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((4, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        mf.mf_moe_finalize(x, torch.zeros((2, 2), dtype=torch.int32),
+                           torch.zeros((2, 2)), torch.zeros((2, 16)),
+                           torch.zeros(16, dtype=torch.bfloat16))

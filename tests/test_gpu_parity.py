@@ -1,0 +1,338 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Bars (from the finalize's determinism requirement and the stated tolerances):
+  - plain finalize residual_out: bit-identical to the oracle (the fp32 FMA chain in fixed
+    order has one correct result);
+  - per-expert and gated residual_out: |gpu - ref| <= 1e-6 + 1e-5 * |ref| (rsqrt / exp
+    rounding makes the fp32 result non-unique);
+  - bf16 outputs: within one bf16 ulp (two neighbours are both correct near a rounding
+    midpoint), and almost always bit-identical.  Where residual_out is not unique, its
+    allowed error passes through the RMSNorm into out, so there the bar is one ulp plus
+    that propagated amount, |gamma| * rms_scale * (1e-6 + 1e-5 * |r|): ~0.003 ulp for a
+    typical element, more only where |r| is near zero;
+  - index handling: exact (covered by the bit-identical residual_out).
+Each case prints its name and launch shape before it runs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import finalize_residual_rmsnorm_amd as mf
+import oracle
+import workloads
+from tests.helpers import bf16_ulp_diff
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def up(a, bf16=False):
+    a = np.ascontiguousarray(a)
+    t = torch.from_numpy(a.view(np.int16) if bf16 else a)
+    if bf16:
+        t = t.view(torch.bfloat16)
+    return t.to(DEV)
+
+
+def bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def assert_bf16_close(gpu, ref, min_exact=0.99):
+    d = bf16_ulp_diff(gpu, ref)
+    assert d.max() <= 1, f"max bf16 ulp diff {d.max()}"
+    assert (d == 0).mean() >= min_exact, f"bit-identical fraction {(d == 0).mean():.5f}"
+
+
+def assert_bf16_close_given_residual_tol(gpu, ref, r_ref, gamma, eps, min_exact=0.99):
+    """bf16 outputs of a non-unique fp32 residual: one ulp plus the propagated tolerance."""
+    og = workloads.bf16_bits_to_f32(gpu).astype(np.float64)
+    orf = workloads.bf16_bits_to_f32(ref).astype(np.float64)
+    r = r_ref.astype(np.float64)
+    scale = 1.0 / np.sqrt((r * r).mean(axis=-1, keepdims=True) + eps)
+    g = np.abs(workloads.bf16_bits_to_f32(gamma).astype(np.float64))
+    mag = np.maximum(np.abs(orf), 2.0 ** -126)
+    ulp = 2.0 ** (np.floor(np.log2(mag)) - 7)
+    allowed = ulp * 1.0001 + 1.01 * g * scale * (1e-6 + 1e-5 * np.abs(r))
+    err = np.abs(og - orf)
+    assert np.all(err <= allowed), f"{(err > allowed).sum()} outputs beyond the bar"
+    d = bf16_ulp_diff(gpu, ref)
+    assert (d == 0).mean() >= min_exact, f"bit-identical fraction {(d == 0).mean():.5f}"
+    say(f"    out: max {d.max()} ulp, {(d > 1).sum()} elements beyond 1 ulp (all near r = 0)")
+
+
+def assert_fp32_tol(gpu, ref):
+    err = np.abs(gpu.astype(np.float64) - ref.astype(np.float64))
+    tol = 1e-6 + 1e-5 * np.abs(ref.astype(np.float64))
+    assert np.all(err <= tol), f"max err {err.max():.3e} ({(err > tol).sum()} over tolerance)"
+    say(f"    residual_out bit-identical fraction {(gpu == ref).mean():.5f}")
+
+
+def finalize_gpu(d, per_expert=False, residual_out=None, out=None):
+    kw = {}
+    if per_expert:
+        kw = dict(expert_ids=up(d["expert_ids"]), expert_gamma=up(d["expert_gamma"], True))
+    return mf.mf_moe_finalize(up(d["expert_rows"], True), up(d["idx"]), up(d["weights"]),
+                              up(d["residual"]), up(d["gamma"], True), d["eps"],
+                              residual_out=residual_out, out=out, **kw)
+
+
+def finalize_ref(d, per_expert=False, tokens=None):
+    sl = slice(None) if tokens is None else tokens
+    args = (d["expert_rows"], d["idx"][sl], d["weights"][sl], d["residual"][sl], d["gamma"],
+            d["eps"])
+    if per_expert:
+        return oracle.moe_finalize(*args, d["expert_ids"][sl], d["expert_gamma"])
+    return oracle.moe_finalize(*args)
+
+
+def shape_str(kind, T, H, k=1):
+    s = mf.mf_launch_shape(kind, T, H, k)
+    return f"wpt={s['waves_per_token']} vpl={s['vectors_per_lane']} block={s['block']} grid={s['grid']}"
+
+
+# ----------------------------------------------------------------------------- finalize
+
+
+def test_finalize_tiny_workload():
+    d = workloads.make_inputs("finalize_tiny")
+    say(f"finalize_tiny T=16 H=1024 k=2: {shape_str(0, 16, 1024, 2)}")
+    out, r = finalize_gpu(d)
+    torch.cuda.synchronize()
+    r_ref, o_ref = finalize_ref(d)
+    assert np.array_equal(r.cpu().numpy(), r_ref)
+    assert_bf16_close(bits(out), o_ref)
+
+
+FINALIZE_SHAPES = [
+    (1, 8, 1, "random"), (3, 24, 2, "random"), (5, 520, 3, "random"),
+    (17, 1024, 8, "expert_sorted"), (33, 4104, 9, "random"), (100, 7168, 8, "expert_sorted"),
+    (2049, 7168, 8, "expert_sorted"), (7, 8192, 16, "random"), (5, 12288, 4, "random"),
+    (3000, 12288, 2, "expert_sorted"), (4, 32768, 3, "random"), (2100, 32768, 1, "random"),
+    (4097, 2048, 5, "expert_sorted"), (6, 3584, 64, "random"),
+]
+
+
+@pytest.mark.parametrize("T,H,k,layout", FINALIZE_SHAPES)
+def test_finalize_matches_oracle(T, H, k, layout):
+    say(f"finalize T={T} H={H} k={k} {layout}: {shape_str(0, T, H, k)}")
+    d = workloads.make_finalize_inputs(T, H, E=max(16, k), k=k, seed=1000 + T + H + k,
+                                       layout=layout)
+    out, r = finalize_gpu(d)
+    torch.cuda.synchronize()
+    r_ref, o_ref = finalize_ref(d)
+    assert np.array_equal(r.cpu().numpy(), r_ref)
+    assert_bf16_close(bits(out), o_ref)
+
+
+@pytest.fixture(scope="module")
+def prefill():
+    say("generating the prefill workload T=16384 H=7168 E=256 k=8 (host, ~20 s)")
+    return workloads.make_inputs("finalize_prefill")
+
+
+def test_finalize_prefill_full_size(prefill):
+    d = prefill
+    T, H = d["T"], d["H"]
+    say(f"finalize_prefill T={T} H={H} k=8: {shape_str(0, T, H, 8)}")
+    rows, idx, w = up(d["expert_rows"], True), up(d["idx"]), up(d["weights"])
+    res, gamma = up(d["residual"]), up(d["gamma"], True)
+    out, r = mf.mf_moe_finalize(rows, idx, w, res, gamma, d["eps"])
+    out2, r2 = mf.mf_moe_finalize(rows, idx, w, res, gamma, d["eps"])
+    torch.cuda.synchronize()
+    assert torch.equal(r, r2) and torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.isfinite(r).all() and torch.isfinite(out.float()).all()
+    # in place on a copy of the residual stream: same bits
+    r3 = res.clone()
+    out3, _ = mf.mf_moe_finalize(rows, idx, w, r3, gamma, d["eps"], residual_out=r3)
+    torch.cuda.synchronize()
+    assert torch.equal(r3, r) and torch.equal(out3.view(torch.int16), out.view(torch.int16))
+    # sampled tokens against the oracle (first, last and random ones)
+    rng = np.random.default_rng(0)
+    tok = np.unique(np.concatenate([np.arange(16), np.arange(T - 16, T),
+                                    rng.choice(T, 96, replace=False)]))
+    r_ref, o_ref = finalize_ref(d, tokens=tok)
+    r_gpu = r.cpu().numpy()[tok]
+    assert np.array_equal(r_gpu, r_ref)
+    assert_bf16_close(bits(out)[tok], o_ref)
+    say(f"    {len(tok)} sampled tokens bit-identical in residual_out")
+
+
+def test_finalize_batch_invariance():
+    # A token's result does not depend on how many tokens share the launch (different
+    # token counts pick different waves-per-token; the reduction tree is the same).
+    d = workloads.make_finalize_inputs(3000, 7168, E=64, k=8, seed=77)
+    say(f"batch invariance H=7168: T=3000 {shape_str(0, 3000, 7168, 8)} vs T=5 {shape_str(0, 5, 7168, 8)}")
+    out_big, r_big = finalize_gpu(d)
+    small = dict(d, T=5, idx=d["idx"][:5], weights=d["weights"][:5], residual=d["residual"][:5])
+    out_small, r_small = finalize_gpu(small)
+    torch.cuda.synchronize()
+    assert torch.equal(r_big[:5], r_small)
+    assert torch.equal(out_big[:5].view(torch.int16), out_small.view(torch.int16))
+
+
+def test_finalize_guard_bands():
+    T, H, k = 37, 520, 3
+    say(f"guard bands T={T} H={H} k={k}: {shape_str(0, T, H, k)}")
+    d = workloads.make_finalize_inputs(T, H, E=8, k=k, seed=78, layout="random")
+    pad = 64
+    rbuf = torch.full((T * H + 2 * pad,), 12345.0, dtype=torch.float32, device=DEV)
+    obuf = torch.full((T * H + 2 * pad,), 0x7BAD, dtype=torch.int16, device=DEV)
+    r_view = rbuf[pad:pad + T * H].view(T, H)
+    o_view = obuf[pad:pad + T * H].view(T, H).view(torch.bfloat16)
+    finalize_gpu(d, residual_out=r_view, out=o_view)
+    torch.cuda.synchronize()
+    assert torch.all(rbuf[:pad] == 12345.0) and torch.all(rbuf[-pad:] == 12345.0)
+    assert torch.all(obuf[:pad] == 0x7BAD) and torch.all(obuf[-pad:] == 0x7BAD)
+    r_ref, o_ref = finalize_ref(d)
+    assert np.array_equal(r_view.cpu().numpy(), r_ref)
+    assert_bf16_close(bits(o_view), o_ref)
+
+
+def test_finalize_on_a_side_stream():
+    d = workloads.make_finalize_inputs(64, 1024, E=8, k=4, seed=79)
+    s = torch.cuda.Stream(device=DEV)
+    with torch.cuda.stream(s):
+        out, r = finalize_gpu(d)
+    s.synchronize()
+    r_ref, o_ref = finalize_ref(d)
+    assert np.array_equal(r.cpu().numpy(), r_ref)
+    assert_bf16_close(bits(out), o_ref)
+
+
+def test_zero_tokens_is_a_no_op():
+    d = workloads.make_finalize_inputs(1, 64, E=4, k=2, seed=80)
+    rows = up(d["expert_rows"], True)
+    out, r = mf.mf_moe_finalize(rows, torch.zeros((0, 2), dtype=torch.int32, device=DEV),
+                                torch.zeros((0, 2), device=DEV), torch.zeros((0, 64), device=DEV),
+                                up(d["gamma"], True))
+    assert out.shape == (0, 64) and r.shape == (0, 64)
+
+
+# ----------------------------------------------------------------------------- per-expert
+
+
+def test_finalize_decode_per_expert_workload():
+    d = workloads.make_inputs("finalize_decode_per_expert")
+    say(f"finalize_decode_per_expert T=64 H=4096 k=8: {shape_str(1, 64, 4096, 8)}")
+    out, r = finalize_gpu(d, per_expert=True)
+    torch.cuda.synchronize()
+    r_ref, o_ref = finalize_ref(d, per_expert=True)
+    assert_fp32_tol(r.cpu().numpy(), r_ref)
+    assert_bf16_close_given_residual_tol(bits(out), o_ref, r_ref, d["gamma"], d["eps"])
+
+
+@pytest.mark.parametrize("T,H,k", [(1, 64, 1), (5, 520, 3), (33, 7168, 8), (2100, 7168, 8),
+                                   (3, 4096, 13), (9, 32768, 2), (2500, 1024, 4)])
+def test_per_expert_matches_oracle(T, H, k):
+    say(f"per-expert T={T} H={H} k={k}: {shape_str(1, T, H, k)}")
+    d = workloads.make_finalize_inputs(T, H, E=32, k=k, seed=2000 + T + H + k, per_expert=True,
+                                       residual_std=2.0)
+    out, r = finalize_gpu(d, per_expert=True)
+    torch.cuda.synchronize()
+    r_ref, o_ref = finalize_ref(d, per_expert=True)
+    assert_fp32_tol(r.cpu().numpy(), r_ref)
+    assert_bf16_close_given_residual_tol(bits(out), o_ref, r_ref, d["gamma"], d["eps"])
+
+
+def test_per_expert_batch_invariance():
+    d = workloads.make_finalize_inputs(2500, 4096, E=32, k=8, seed=81, per_expert=True)
+    say(f"per-expert batch invariance: T=2500 {shape_str(1, 2500, 4096, 8)} vs T=3 {shape_str(1, 3, 4096, 8)}")
+    out_big, r_big = finalize_gpu(d, per_expert=True)
+    small = dict(d, T=3, idx=d["idx"][:3], weights=d["weights"][:3], residual=d["residual"][:3],
+                 expert_ids=d["expert_ids"][:3])
+    out_small, r_small = finalize_gpu(small, per_expert=True)
+    torch.cuda.synchronize()
+    assert torch.equal(r_big[:3], r_small)
+    assert torch.equal(out_big[:3].view(torch.int16), out_small.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- gated
+
+
+def gated_gpu(d, residual_out=None):
+    return mf.mf_gated_residual_rmsnorm(up(d["x"], True), up(d["gate"], True), up(d["residual"]),
+                                        up(d["gamma"], True), d["eps"], residual_out=residual_out)
+
+
+def test_gated_workload_full_size():
+    d = workloads.make_inputs("gated_residual_rmsnorm")
+    say(f"gated T=4096 H=8192: {shape_str(2, 4096, 8192)}")
+    out, r = gated_gpu(d)
+    torch.cuda.synchronize()
+    r_ref, o_ref = oracle.gated_residual_rmsnorm(d["x"], d["gate"], d["residual"], d["gamma"],
+                                                 d["eps"])
+    assert_fp32_tol(r.cpu().numpy(), r_ref)
+    assert_bf16_close_given_residual_tol(bits(out), o_ref, r_ref, d["gamma"], d["eps"])
+
+
+@pytest.mark.parametrize("T,H", [(1, 8), (3, 520), (5000, 1024), (7, 32768), (2049, 8192)])
+def test_gated_matches_oracle(T, H):
+    say(f"gated T={T} H={H}: {shape_str(2, T, H)}")
+    d = workloads.make_gated_inputs(T, H, seed=3000 + T + H)
+    out, r = gated_gpu(d)
+    torch.cuda.synchronize()
+    r_ref, o_ref = oracle.gated_residual_rmsnorm(d["x"], d["gate"], d["residual"], d["gamma"],
+                                                 d["eps"])
+    assert_fp32_tol(r.cpu().numpy(), r_ref)
+    assert_bf16_close_given_residual_tol(bits(out), o_ref, r_ref, d["gamma"], d["eps"])
+
+
+def test_gated_zero_gate_is_exact():
+    # sigmoid(0) = 1/2 exactly, so residual_out = fp32(residual + x/2) bit for bit.
+    d = workloads.make_gated_inputs(64, 8192, seed=82)
+    d["gate"] = np.zeros_like(d["gate"])
+    out, r = gated_gpu(d)
+    torch.cuda.synchronize()
+    want = d["residual"] + np.float32(0.5) * workloads.bf16_bits_to_f32(d["x"])
+    assert np.array_equal(r.cpu().numpy(), want)
+
+
+def test_gated_in_place():
+    d = workloads.make_gated_inputs(100, 8192, seed=83)
+    res = up(d["residual"])
+    out, _ = mf.mf_gated_residual_rmsnorm(up(d["x"], True), up(d["gate"], True), res,
+                                          up(d["gamma"], True), d["eps"], residual_out=res)
+    out2, r2 = gated_gpu(d)
+    torch.cuda.synchronize()
+    assert torch.equal(res, r2) and torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- per-head
+
+
+def test_per_head_workload_full_size():
+    d = workloads.make_inputs("rmsnorm_sigmoid_gate")
+    say("per-head T=4096 heads=64 D=64")
+    out = mf.mf_rmsnorm_sigmoid_gate(up(d["x"], True), up(d["gate"], True), up(d["gamma"], True),
+                                     d["eps"])
+    torch.cuda.synchronize()
+    o_ref = oracle.rmsnorm_sigmoid_gate(d["x"], d["gate"], d["gamma"], d["eps"])
+    assert_bf16_close(bits(out), o_ref)
+
+
+@pytest.mark.parametrize("T,heads", [(1, 1), (3, 5), (7, 64), (1000, 3)])
+def test_per_head_ragged(T, heads):
+    say(f"per-head T={T} heads={heads}")
+    d = workloads.make_per_head_inputs(T, heads, 64, seed=4000 + T + heads)
+    out = mf.mf_rmsnorm_sigmoid_gate(up(d["x"], True), up(d["gate"], True), up(d["gamma"], True),
+                                     d["eps"])
+    torch.cuda.synchronize()
+    o_ref = oracle.rmsnorm_sigmoid_gate(d["x"], d["gate"], d["gamma"], d["eps"])
+    assert_bf16_close(bits(out), o_ref, min_exact=0.98)
+
+
+# ----------------------------------------------------------------------------- copy
+
+
+def test_stream_copy():
+    src = torch.randint(-2**31, 2**31 - 1, (1 << 20,), dtype=torch.int32, device=DEV)
+    dst = torch.zeros_like(src)
+    mf.mf_stream_copy(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
