@@ -10,16 +10,16 @@
 //
 // How it maps onto CDNA4 (the pages' kernels are CuTe-DSL / cluster designs for other
 // hardware; none of that carries over):
-//  - One token row per `wpt` wavefronts (wpt = 1 when there are enough tokens to fill the
-//    chip); each lane keeps its slice of the row in fp32 registers from the first FMA to the
-//    bf16 store, so the residual is read once and written once, and nothing is re-read.
-//  - Gathers are 16-byte loads, a full 1 KiB per wave instruction, contiguous within a row.
-//    All loads of a batch of JB rows are issued before any is consumed (JB * VPL vectors in
-//    flight per lane).
-//  - The token's idx / weight / expert id are wave-uniform scalar loads.
+//  - One workgroup per token; its waves split the row into 1 KiB slots (row_norm.h) and keep
+//    their part of the row in fp32 registers from the first FMA to the bf16 store, so the
+//    residual is read once and written once and nothing is re-read.
+//  - Gathers are 16-byte loads, a full contiguous 1 KiB per wave instruction.  A batch of
+//    rows is issued in full before any of it is used; with the compile-time top-k (k = 8)
+//    the token's indices and weights come in a few wide scalar loads and all k rows, the
+//    residual and gamma are in flight at once, so a token costs about one memory round trip.
 //  - No MFMA: the arithmetic intensity is below 1 flop per byte; the kernel is bound by HBM.
-//  - No atomics and a fixed reduction tree: results are bit-deterministic and do not depend
-//    on the launch shape.
+//  - No atomics and a fixed reduction order: results are bit-deterministic and identical for
+//    a token whatever batch it is in.
 #pragma once
 
 #include "row_norm.h"
@@ -41,151 +41,159 @@ struct FinalizeArgs {
     int32_t H;
     int32_t k;
     int32_t num_experts;
-    int32_t wpt;                 // waves per token (power of two)
-    int32_t spw;                 // slots per wave
     float eps;
 };
 
-// Rows per gather batch: enough 16-byte loads in flight per lane without spilling.  The
-// per-expert variant also holds the batch's gamma rows, so it batches less at larger VPL.
-constexpr int gather_batch_for(int vpl, bool per_expert) {
-    return vpl >= 8 ? 1 : (vpl >= 4 ? (per_expert ? 1 : 2) : (vpl >= 2 ? 4 : 8));
+// Rows gathered per batch: up to 16 vectors per lane in flight (fewer for wider slices and
+// for the per-expert variant, which also loads each row's expert gamma), at most the
+// compile-time top-k.
+constexpr int batch_rows(int vpl, int kc, bool per_expert) {
+    const int vectors = per_expert ? (vpl == 1 && kc > 0 ? 8 : 4) : (vpl <= 2 ? 16 : 8);
+    const int jb = vectors / vpl;
+    const int j1 = jb < 1 ? 1 : (jb > 8 ? 8 : jb);
+    return kc > 0 && j1 > kc ? kc : j1;
 }
 
-// The per-expert variant is launched with at most 8 waves per token (512 threads).
-constexpr int finalize_block_max(int vpl, bool per_expert) {
-    return per_expert && block_max_for(vpl) > 512 ? 512 : block_max_for(vpl);
+// Workgroup bound (16 waves; 8 for the per-expert variant) and the minimum waves per SIMD
+// the register allocation must allow.  One slot per wave keeps the plain kernel within 64
+// VGPRs, so two workgroups of 16 waves share a CU.
+constexpr int finalize_block_max(bool per_expert) { return per_expert ? 512 : 1024; }
+constexpr int finalize_min_waves(int vpl, bool per_expert) {
+    return per_expert ? 2 : (vpl == 1 ? 8 : 4);
 }
 
-template <int VPL, bool PER_EXPERT>
-__global__ void __launch_bounds__(finalize_block_max(VPL, PER_EXPERT))
+// One gather batch: JB rows (and, per-expert, their gamma rows) of the lane's slots.
+template <int VPL, int JB, bool PER_EXPERT>
+struct GatherBatch {
+    u32x4 x[JB][VPL];
+    u32x4 g[PER_EXPERT ? JB : 1][VPL];
+};
+
+template <int VPL, int JB, bool PER_EXPERT, int TAIL>
+__device__ __forceinline__ void issue_batch(GatherBatch<VPL, JB, PER_EXPERT>& b,
+                                            const FinalizeArgs& a, int64_t tk, int jb, int k,
+                                            const Slots<VPL, TAIL>& sl) {
+    const int64_t last_row = a.num_rows - 1;
+#pragma unroll
+    for (int u = 0; u < JB; ++u) {
+        // Past the last j of a partial batch, reload row k-1 (same cache lines; unused).
+        const int j = min(jb + u, k - 1);
+        int64_t row = a.idx[tk + j];
+        row = row < 0 ? 0 : (row > last_row ? last_row : row);
+        const uint16_t* rp = a.rows + row * a.H;
+#pragma unroll
+        for (int s = 0; s < VPL; ++s)
+            b.x[u][s] = sl.suni[s] ? ld_stream(at<u32x4>(rp, sl.eoff[s] * 2u)) : u32x4{0u, 0u, 0u, 0u};
+        if constexpr (PER_EXPERT) {
+            int e = a.eids[tk + j];
+            e = e < 0 ? 0 : (e >= a.num_experts ? a.num_experts - 1 : e);
+            const uint16_t* gp = a.egamma + (int64_t)e * a.H;
+#pragma unroll
+            for (int s = 0; s < VPL; ++s) b.g[u][s] = *at<u32x4>(gp, sl.eoff[s] * 2u);
+        }
+    }
+}
+
+// acc += w_j * row_j for the batch's rows in ascending j (per-expert: row_j normalised with
+// its own mean square and multiplied by its expert's gamma first).
+template <int VPL, int JB, bool PER_EXPERT, int TAIL>
+__device__ __forceinline__ void consume_batch(const GatherBatch<VPL, JB, PER_EXPERT>& b,
+                                              float (&acc)[VPL][8], const FinalizeArgs& a,
+                                              int64_t tk, int jb, int k,
+                                              const Slots<VPL, TAIL>& sl, TokenLds& L,
+                                              const RowMap& m) {
+    float inv[JB];
+    if constexpr (PER_EXPERT) {
+#pragma unroll
+        for (int u = 0; u < JB; ++u) {
+            float x[VPL][8];
+#pragma unroll
+            for (int s = 0; s < VPL; ++s) widen8(b.x[u][s], x[s]);
+            inv[u] = lane_sumsq(x, sl);
+        }
+        token_sum<JB>(inv, L, m);
+#pragma unroll
+        for (int u = 0; u < JB; ++u) inv[u] = 1.0f / __builtin_sqrtf(inv[u] / (float)a.H + a.eps);
+    }
+#pragma unroll
+    for (int u = 0; u < JB; ++u) {
+        if (jb + u < k) {
+            const float wj = a.w[tk + jb + u];
+#pragma unroll
+            for (int s = 0; s < VPL; ++s) {
+                float x[8];
+                widen8(b.x[u][s], x);
+                if constexpr (PER_EXPERT) {
+                    float g[8];
+                    widen8(b.g[u][s], g);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        acc[s][i] = __builtin_fmaf(wj, (x[i] * inv[u]) * g[i], acc[s][i]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[s][i] = __builtin_fmaf(wj, x[i], acc[s][i]);
+                }
+            }
+        }
+    }
+}
+
+// KC: the top-k fixed at compile time (8), or 0 for a runtime k.
+template <int VPL, int KC, bool PER_EXPERT, int TAIL>
+__global__ void __launch_bounds__(finalize_block_max(PER_EXPERT))
+__attribute__((amdgpu_waves_per_eu(finalize_min_waves(VPL, PER_EXPERT), 8)))
 moe_finalize_kernel(const FinalizeArgs a) {
-    constexpr int JB = gather_batch_for(VPL, PER_EXPERT);
-    constexpr int NP = next_pow2(VPL);
-    constexpr int WPT_MAX = wpt_max_for(VPL);
+    constexpr int JB = batch_rows(VPL, KC, PER_EXPERT);
+    // With small row slices the residual and gamma ride along with the first batch.
+    constexpr bool EARLY = VPL <= 2;
     extern __shared__ float lds[];
 
-    const RowMap m = row_map(a.T, a.wpt);
-    if (a.wpt == 1 && !m.valid) return;  // no barriers when wpt == 1
-
+    const RowMap m = row_map();
     const int H = a.H;
-    int eoff[VPL];
-    bool sval[VPL];
-#pragma unroll
-    for (int s = 0; s < VPL; ++s) {
-        const int e = (m.wit * a.spw + s) * kSlot + m.lane * kVec;
-        sval[s] = e < H;
-        eoff[s] = sval[s] ? e : 0;
-    }
+    const int k = KC > 0 ? KC : a.k;
+    const Slots<VPL, TAIL> sl = slot_offsets<VPL, TAIL>(m, H);
+    const int64_t tk = m.t * k;
+    const float* res = a.residual + m.t * H;
 
-    const int64_t tk = m.t * a.k;
-    const int64_t last_row = a.num_rows - 1;
     float acc[VPL][8];
 #pragma unroll
     for (int s = 0; s < VPL; ++s)
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[s][i] = 0.0f;
+    f32x4 rv[VPL][2];
+    u32x4 g[VPL];
+    auto load_res_gamma = [&]() {
+#pragma unroll
+        for (int s = 0; s < VPL; ++s) {
+            rv[s][0] = ld_stream(at<f32x4>(res, sl.eoff[s] * 4u));
+            rv[s][1] = ld_stream(at<f32x4>(res, sl.eoff[s] * 4u + 16u));
+        }
+        load_gamma(g, a.gamma, sl);
+    };
 
-    int parity = 0;
-    for (int jb = 0; jb < a.k; jb += JB) {
-        u32x4 xv[JB][VPL];
-#pragma unroll
-        for (int u = 0; u < JB; ++u) {
-            // Past the last j of a partial batch, reload row k-1 (same cache lines; unused).
-            const int j = min(jb + u, a.k - 1);
-            int64_t row = a.idx[tk + j];
-            row = row < 0 ? 0 : (row > last_row ? last_row : row);
-            const uint16_t* rp = a.rows + row * H;
-#pragma unroll
-            for (int s = 0; s < VPL; ++s)
-                xv[u][s] = ld_stream(reinterpret_cast<const u32x4*>(rp + eoff[s]));
-        }
-        if constexpr (PER_EXPERT) {
-            // RMSNorm of each gathered row with its expert's gamma, before the weighted sum.
-            u32x4 gv[JB][VPL];
-            float ps[JB];
-#pragma unroll
-            for (int u = 0; u < JB; ++u) {
-                const int j = min(jb + u, a.k - 1);
-                int e = a.eids[tk + j];
-                e = e < 0 ? 0 : (e >= a.num_experts ? a.num_experts - 1 : e);
-                const uint16_t* gp = a.egamma + (int64_t)e * H;
-#pragma unroll
-                for (int s = 0; s < VPL; ++s)
-                    gv[u][s] = *reinterpret_cast<const u32x4*>(gp + eoff[s]);
-                float p[NP];
-#pragma unroll
-                for (int s = 0; s < NP; ++s) p[s] = 0.0f;
-#pragma unroll
-                for (int s = 0; s < VPL; ++s) {
-                    float x[8];
-                    widen8(xv[u][s], x);
-                    p[s] = sval[s] ? sumsq8(x) : 0.0f;
-                }
-                ps[u] = tree_sum<NP>(p);
-            }
-            token_sum<JB, WPT_MAX>(ps, lds, parity, m);
-#pragma unroll
-            for (int u = 0; u < JB; ++u) {
-                if (jb + u < a.k) {
-                    const float inv = 1.0f / __builtin_sqrtf(ps[u] / (float)H + a.eps);
-                    const float wj = a.w[tk + jb + u];
-#pragma unroll
-                    for (int s = 0; s < VPL; ++s) {
-                        float x[8], g[8];
-                        widen8(xv[u][s], x);
-                        widen8(gv[u][s], g);
-#pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            acc[s][i] = __builtin_fmaf(wj, (x[i] * inv) * g[i], acc[s][i]);
-                    }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < JB; ++u) {
-                if (jb + u < a.k) {
-                    const float wj = a.w[tk + jb + u];
-#pragma unroll
-                    for (int s = 0; s < VPL; ++s) {
-                        float x[8];
-                        widen8(xv[u][s], x);
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) acc[s][i] = __builtin_fmaf(wj, x[i], acc[s][i]);
-                    }
-                }
-            }
-        }
+    TokenLds L = token_lds(lds, m.wpt, PER_EXPERT ? JB : 1);
+    constexpr int UNROLL = KC > 0 ? (KC + JB - 1) / JB : 1;
+#pragma unroll UNROLL
+    for (int jb = 0; jb < k; jb += JB) {
+        GatherBatch<VPL, JB, PER_EXPERT> b;
+        issue_batch(b, a, tk, jb, k, sl);
+        if (EARLY && jb == 0) load_res_gamma();
+        consume_batch(b, acc, a, tk, jb, k, sl, L, m);
     }
+    if (!EARLY) load_res_gamma();
 
     // Residual add (one fp32 add after the k-term sum), then the store of the updated
     // residual.  Every residual load precedes every residual_out store in program order, so
     // the in-place case (residual_out == residual) never orders a load behind a store.
-    const float* res = a.residual + m.t * H;
-    float* res_out = a.residual_out + m.t * H;
 #pragma unroll
-    for (int s = 0; s < VPL; ++s) {
-        const f32x4 r0 = ld_stream(reinterpret_cast<const f32x4*>(res + eoff[s]));
-        const f32x4 r1 = ld_stream(reinterpret_cast<const f32x4*>(res + eoff[s] + 4));
+    for (int s = 0; s < VPL; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            acc[s][i] = r0[i] + acc[s][i];
-            acc[s][4 + i] = r1[i] + acc[s][4 + i];
+            acc[s][i] = rv[s][0][i] + acc[s][i];
+            acc[s][4 + i] = rv[s][1][i] + acc[s][4 + i];
         }
-    }
-    if (m.valid) {
-#pragma unroll
-        for (int s = 0; s < VPL; ++s) {
-            if (sval[s]) {
-                st_stream(f32x4{acc[s][0], acc[s][1], acc[s][2], acc[s][3]},
-                          reinterpret_cast<f32x4*>(res_out + eoff[s]));
-                st_stream(f32x4{acc[s][4], acc[s][5], acc[s][6], acc[s][7]},
-                          reinterpret_cast<f32x4*>(res_out + eoff[s] + 4));
-            }
-        }
-    }
-
-    rmsnorm_store<VPL>(acc, eoff, sval, a.gamma, a.out + m.t * H, H, a.eps, lds, parity, m);
+    store_residual(acc, sl, a.residual_out + m.t * H);
+    rmsnorm_store(acc, g, sl, a.out + m.t * H, H, a.eps, L, m);
 }
 
 }  // namespace mf

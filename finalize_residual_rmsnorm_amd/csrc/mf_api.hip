@@ -2,6 +2,7 @@
 // launch-shape selection and kernel dispatch.  Stateless and allocation-free.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -14,15 +15,13 @@ namespace {
 
 using namespace mf;
 
-constexpr int32_t kMaxH = 32768;       // 64 slots of 512 values
+constexpr int32_t kMaxH = 32768;   // 64 slots of 512 values
 constexpr int32_t kMaxK = 64;
-constexpr int kMaxVpl = 16;
-constexpr int kMaxVplPerExpert = 8;  // the per-expert variant also holds a batch of gamma rows
-constexpr int kMaxWptPerExpert = 8;  // keeps its LDS (a batch of sums per wave) under 64 KiB
-constexpr int kMaxWpt = 16;
-// Waves that keep all 256 CUs of an MI355X busy (8 per CU); smaller token counts spread
-// each row over more waves instead.
-constexpr int64_t kFillWaves = 2048;
+constexpr int kMaxWaves = 16;           // waves per workgroup (1024 threads)
+constexpr int kMaxWavesPerExpert = 8;   // the per-expert variant reduces a batch of row sums
+                                        // per barrier; 8 waves keep that LDS under 64 KiB
+constexpr int kMaxVpl = 4;              // plain finalize and gated kernels: 4 x 16 x 512 = 32768
+constexpr int kMaxVplPerExpert = 8;     // per-expert finalize: 8 x 8 x 512 = 32768
 constexpr int kPerHeadGroupsPerWave = 2;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -36,84 +35,129 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 bool eps_ok(float eps) { return std::isfinite(eps) && eps >= 0.0f; }
 
+bool row_width_supported(int32_t H) { return H >= 8 && H <= kMaxH && H % 8 == 0; }
+
+// Launch shape of the token-row kernels: one workgroup per token, `wpt` waves holding `vpl`
+// slots each.  It depends on H only, so a token's result never depends on the batch.
 struct RowShape {
-    int wpt;        // waves per token (power of two)
-    int spw;        // slots per wave
-    int vpl;        // slots held per lane (kernel instantiation)
+    int tail;       // RowTail: how the row's last slot meets H
+    int vpl;        // slots per wave (kernel instantiation)
+    int wpt;        // waves per token = per workgroup
     int block;      // threads per workgroup
-    int64_t grid;   // workgroups
+    int64_t grid;   // workgroups = tokens
+    int nr;         // row sums per reduction barrier
     size_t lds;     // dynamic LDS bytes
 };
 
-bool row_shape_supported(int32_t H) { return H >= 8 && H <= kMaxH && H % 8 == 0; }
+int pow2_at_least(int n) {
+    int p = 1;
+    while (p < n) p *= 2;
+    return p;
+}
 
-// Launch shape of the token-row kernels.  The per-expert variant reduces one row sum per
-// gathered row of a batch at each barrier, so its LDS holds a batch of sums per wave.
-RowShape row_shape(int64_t T, int32_t H, bool per_expert) {
+// One slot of 512 values per wave, unless the row needs more than max_waves waves; never more
+// than max_vpl slots per wave (the widest compiled instantiation).
+RowShape row_shape(int64_t T, int32_t H, int max_waves, int max_vpl) {
     const int ns = (H + kSlot - 1) / kSlot;
-    int nsp = 1;
-    while (nsp < ns) nsp *= 2;
-    int wpt = 1;
-    const int max_vpl = per_expert ? kMaxVplPerExpert : kMaxVpl;
-    while (nsp / wpt > max_vpl) wpt *= 2;                   // the row must fit in registers
-    const int wpt_cap = per_expert ? kMaxWptPerExpert : kMaxWpt;
-    while (wpt < nsp && wpt < wpt_cap && T * wpt < kFillWaves) wpt *= 2;  // fill the chip
+    // Waves per token are a power of two (measured faster on MI355X than an odd wave count;
+    // spare waves hold slots past H and skip their loads).  Among the slots-per-wave values
+    // that fit in 16 waves, take the one that leaves the fewest spare slots, then the
+    // smallest.
+    const int vmin = (ns + max_waves - 1) / max_waves;
+    int best_v = vmin, best_waste = 1 << 30;
+    for (int v = vmin; v <= std::min(vmin + 2, max_vpl); ++v) {
+        const int waste = pow2_at_least((ns + v - 1) / v) * v - ns;
+        if (waste < best_waste) {
+            best_v = v;
+            best_waste = waste;
+        }
+    }
     RowShape s;
-    s.wpt = wpt;
-    s.spw = nsp / wpt;
-    s.vpl = wpt == 1 ? ns : s.spw;
-    const int tpb = wpt >= 4 ? 1 : 4 / wpt;
-    s.block = kWave * wpt * tpb;
-    s.grid = (T + tpb - 1) / tpb;
-    const int nr = per_expert ? gather_batch_for(s.vpl, true) : 1;
-    s.lds = wpt > 1 ? token_sum_lds_bytes(s.block / kWave, nr) : 0;
+    s.vpl = best_v;
+    s.wpt = pow2_at_least((ns + s.vpl - 1) / s.vpl);
+    s.tail = H != ns * kSlot ? kRowRagged : (ns == s.wpt * s.vpl ? kRowFull : kRowWhole);
+    s.block = kWave * s.wpt;
+    s.grid = T;
+    s.nr = 1;
+    s.lds = token_sum_lds_bytes(s.wpt, 1);
     return s;
 }
 
-template <int VPL, bool PE>
-hipError_t launch_finalize_vpl(const FinalizeArgs& a, const RowShape& s, hipStream_t st) {
-    void* args[] = {const_cast<FinalizeArgs*>(&a)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&moe_finalize_kernel<VPL, PE>),
-                           dim3((unsigned)s.grid), dim3(s.block), args, s.lds, st);
+// The top-k the finalize kernels are specialised for (all loads of a token issued at once).
+constexpr int kCompiledTopK = 8;
+
+constexpr bool uses_compiled_topk(int vpl, bool per_expert);
+
+RowShape finalize_shape(int64_t T, int32_t H, int32_t k, bool per_expert) {
+    RowShape s = per_expert ? row_shape(T, H, kMaxWavesPerExpert, kMaxVplPerExpert)
+                            : row_shape(T, H, kMaxWaves, kMaxVpl);
+    const int kc = k == kCompiledTopK && uses_compiled_topk(s.vpl, per_expert) ? kCompiledTopK : 0;
+    s.nr = per_expert ? batch_rows(s.vpl, kc, true) : 1;
+    s.lds = token_sum_lds_bytes(s.wpt, s.nr);
+    return s;
 }
 
-hipError_t launch_finalize(bool per_expert, const FinalizeArgs& a, const RowShape& s,
-                           hipStream_t st) {
-#define MF_CASE(V, PE) \
-    case V: return launch_finalize_vpl<V, PE>(a, s, st);
+template <int VPL, int KC, bool PE>
+const void* finalize_fn(int tail) {
+    switch (tail) {
+        case kRowFull: return reinterpret_cast<const void*>(&moe_finalize_kernel<VPL, KC, PE, kRowFull>);
+        case kRowWhole: return reinterpret_cast<const void*>(&moe_finalize_kernel<VPL, KC, PE, kRowWhole>);
+        default: return reinterpret_cast<const void*>(&moe_finalize_kernel<VPL, KC, PE, kRowRagged>);
+    }
+}
+
+// The fully unrolled top-k keeps every row of a token in flight; it fits in registers up to
+// two slots per wave (one for the per-expert variant, which also holds a gamma row per
+// gathered row).  Wider slices keep the batched loop.
+constexpr bool uses_compiled_topk(int vpl, bool per_expert) { return vpl <= (per_expert ? 1 : 2); }
+
+template <int VPL, bool PE>
+const void* finalize_fn(int tail, int k) {
+    if constexpr (uses_compiled_topk(VPL, PE)) {
+        if (k == kCompiledTopK) return finalize_fn<VPL, kCompiledTopK, PE>(tail);
+    }
+    return finalize_fn<VPL, 0, PE>(tail);
+}
+
+const void* finalize_kernel_for(const RowShape& s, int k, bool per_expert) {
     if (per_expert) {
         switch (s.vpl) {
-            MF_CASE(1, true) MF_CASE(2, true) MF_CASE(3, true) MF_CASE(4, true)
-            MF_CASE(5, true) MF_CASE(6, true) MF_CASE(7, true) MF_CASE(8, true)
-            default: return hipErrorInvalidValue;
+            case 1: return finalize_fn<1, true>(s.tail, k);
+            case 2: return finalize_fn<2, true>(s.tail, k);
+            case 3: return finalize_fn<3, true>(s.tail, k);
+            case 4: return finalize_fn<4, true>(s.tail, k);
+            case 5: return finalize_fn<5, true>(s.tail, k);
+            case 6: return finalize_fn<6, true>(s.tail, k);
+            case 7: return finalize_fn<7, true>(s.tail, k);
+            case 8: return finalize_fn<8, true>(s.tail, k);
+            default: return nullptr;
         }
     }
     switch (s.vpl) {
-        MF_CASE(1, false) MF_CASE(2, false) MF_CASE(3, false) MF_CASE(4, false)
-        MF_CASE(5, false) MF_CASE(6, false) MF_CASE(7, false) MF_CASE(8, false)
-        MF_CASE(9, false) MF_CASE(10, false) MF_CASE(11, false) MF_CASE(12, false)
-        MF_CASE(13, false) MF_CASE(14, false) MF_CASE(15, false) MF_CASE(16, false)
-        default: return hipErrorInvalidValue;
+        case 1: return finalize_fn<1, false>(s.tail, k);
+        case 2: return finalize_fn<2, false>(s.tail, k);
+        case 3: return finalize_fn<3, false>(s.tail, k);
+        case 4: return finalize_fn<4, false>(s.tail, k);
+        default: return nullptr;
     }
-#undef MF_CASE
 }
 
 template <int VPL>
-hipError_t launch_gated_vpl(const GatedArgs& a, const RowShape& s, hipStream_t st) {
-    void* args[] = {const_cast<GatedArgs*>(&a)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&gated_residual_rmsnorm_kernel<VPL>),
-                           dim3((unsigned)s.grid), dim3(s.block), args, s.lds, st);
+const void* gated_fn(int tail) {
+    switch (tail) {
+        case kRowFull: return reinterpret_cast<const void*>(&gated_residual_rmsnorm_kernel<VPL, kRowFull>);
+        case kRowWhole: return reinterpret_cast<const void*>(&gated_residual_rmsnorm_kernel<VPL, kRowWhole>);
+        default: return reinterpret_cast<const void*>(&gated_residual_rmsnorm_kernel<VPL, kRowRagged>);
+    }
 }
 
-hipError_t launch_gated(const GatedArgs& a, const RowShape& s, hipStream_t st) {
+const void* gated_kernel_for(const RowShape& s) {
     switch (s.vpl) {
-#define MF_CASE(V) \
-    case V: return launch_gated_vpl<V>(a, s, st);
-        MF_CASE(1) MF_CASE(2) MF_CASE(3) MF_CASE(4) MF_CASE(5) MF_CASE(6) MF_CASE(7) MF_CASE(8)
-        MF_CASE(9) MF_CASE(10) MF_CASE(11) MF_CASE(12) MF_CASE(13) MF_CASE(14) MF_CASE(15)
-        MF_CASE(16)
-#undef MF_CASE
-        default: return hipErrorInvalidValue;
+        case 1: return gated_fn<1>(s.tail);
+        case 2: return gated_fn<2>(s.tail);
+        case 3: return gated_fn<3>(s.tail);
+        case 4: return gated_fn<4>(s.tail);
+        default: return nullptr;
     }
 }
 
@@ -130,20 +174,23 @@ extern "C" {
 
 int mf_moe_finalize_supported(int32_t H, int32_t k, int per_expert) {
     (void)per_expert;
-    return row_shape_supported(H) && k >= 1 && k <= kMaxK;
+    return row_width_supported(H) && k >= 1 && k <= kMaxK;
 }
 
-int mf_gated_residual_rmsnorm_supported(int32_t H) { return row_shape_supported(H); }
+int mf_gated_residual_rmsnorm_supported(int32_t H) { return row_width_supported(H); }
 
 int mf_rmsnorm_sigmoid_gate_supported(int32_t head_dim) { return head_dim == kHeadDim; }
 
 int mf_launch_shape(int kind, int64_t T, int32_t H, int32_t k, int32_t* waves_per_token,
                     int32_t* vectors_per_lane, int32_t* block_threads, int64_t* grid_blocks) {
     if (kind < 0 || kind > 2 || T < 0) return MF_ERR_SHAPE;
-    if (kind <= 1 ? !mf_moe_finalize_supported(H, k, kind) : !row_shape_supported(H))
+    if (kind <= 1 ? !mf_moe_finalize_supported(H, k, kind) : !row_width_supported(H))
         return MF_ERR_UNSUPPORTED;
-    const RowShape s = row_shape(T, H, kind == 1);
+    const RowShape s = kind <= 1 ? finalize_shape(T, H, k, kind == 1) : row_shape(T, H, kMaxWaves, kMaxVpl);
     if (T > 0 && !grid_fits(s.grid, s.block)) return MF_ERR_SHAPE;
+    // the same kernel lookup as the launch itself
+    const void* fn = kind <= 1 ? finalize_kernel_for(s, k, kind == 1) : gated_kernel_for(s);
+    if (!fn || (kind <= 1 && s.block > finalize_block_max(kind == 1))) return MF_ERR_UNSUPPORTED;
     if (waves_per_token) *waves_per_token = s.wpt;
     if (vectors_per_lane) *vectors_per_lane = s.vpl;
     if (block_threads) *block_threads = s.block;
@@ -160,8 +207,10 @@ int mf_moe_finalize(const uint16_t* expert_rows, int64_t num_rows, const int32_t
     const bool per_expert = expert_ids != nullptr || expert_gamma != nullptr;
     if (!mf_moe_finalize_supported(H, k, per_expert)) return MF_ERR_UNSUPPORTED;
     if (T == 0) return MF_OK;
-    const RowShape s = row_shape(T, H, per_expert);
+    const RowShape s = finalize_shape(T, H, k, per_expert);
     if (!grid_fits(s.grid, s.block)) return MF_ERR_SHAPE;
+    const void* fn = finalize_kernel_for(s, k, per_expert);
+    if (!fn || s.block > finalize_block_max(per_expert)) return MF_ERR_UNSUPPORTED;
     if (!expert_rows || !idx || !weights || !residual || !residual_out || !gamma || !out)
         return MF_ERR_NULL;
     if (per_expert && (!expert_ids || !expert_gamma)) return MF_ERR_NULL;
@@ -204,21 +253,22 @@ int mf_moe_finalize(const uint16_t* expert_rows, int64_t num_rows, const int32_t
     a.H = H;
     a.k = k;
     a.num_experts = per_expert ? num_experts : 0;
-    a.wpt = s.wpt;
-    a.spw = s.spw;
     a.eps = eps;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    return hip_status(launch_finalize(per_expert, a, s, st));
+    void* args[] = {&a};
+    return hip_status(hipLaunchKernel(fn, dim3((unsigned)s.grid), dim3(s.block), args, s.lds,
+                                      reinterpret_cast<hipStream_t>(stream)));
 }
 
 int mf_gated_residual_rmsnorm(const uint16_t* x, const uint16_t* gate, const float* residual,
                               float* residual_out, const uint16_t* gamma, float eps,
                               uint16_t* out, int64_t T, int32_t H, void* stream) {
     if (T < 0) return MF_ERR_SHAPE;
-    if (!row_shape_supported(H)) return MF_ERR_UNSUPPORTED;
+    if (!row_width_supported(H)) return MF_ERR_UNSUPPORTED;
     if (T == 0) return MF_OK;
-    const RowShape s = row_shape(T, H, false);
+    const RowShape s = row_shape(T, H, kMaxWaves, kMaxVpl);
     if (!grid_fits(s.grid, s.block)) return MF_ERR_SHAPE;
+    const void* fn = gated_kernel_for(s);
+    if (!fn) return MF_ERR_UNSUPPORTED;
     if (!x || !gate || !residual || !residual_out || !gamma || !out) return MF_ERR_NULL;
     if (!eps_ok(eps)) return MF_ERR_VALUE;
     if (!aligned(x, 16) || !aligned(gate, 16) || !aligned(residual, 16) ||
@@ -246,10 +296,10 @@ int mf_gated_residual_rmsnorm(const uint16_t* x, const uint16_t* gate, const flo
     a.out = out;
     a.T = T;
     a.H = H;
-    a.wpt = s.wpt;
-    a.spw = s.spw;
     a.eps = eps;
-    return hip_status(launch_gated(a, s, reinterpret_cast<hipStream_t>(stream)));
+    void* args[] = {&a};
+    return hip_status(hipLaunchKernel(fn, dim3((unsigned)s.grid), dim3(s.block), args, s.lds,
+                                      reinterpret_cast<hipStream_t>(stream)));
 }
 
 int mf_rmsnorm_sigmoid_gate(const uint16_t* x, const uint16_t* gate, const uint16_t* gamma,

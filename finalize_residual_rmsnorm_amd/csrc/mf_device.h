@@ -36,6 +36,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// Address `base + byte_off` with a 32-bit unsigned offset: with a wave-uniform base this is
+// the SGPR-base + VGPR-offset form of global loads/stores (no 64-bit address per lane).
+template <class T>
+__device__ __forceinline__ const T* at(const void* base, uint32_t byte_off) {
+    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+template <class T>
+__device__ __forceinline__ T* at(void* base, uint32_t byte_off) {
+    return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + byte_off);
+}
+
 // Single-use streams (gathered rows, residual in/out, outputs) bypass cache retention.
 template <class T>
 __device__ __forceinline__ T ld_stream(const T* p) { return __builtin_nontemporal_load(p); }
@@ -67,17 +78,6 @@ __device__ __forceinline__ float wave_sum(float v) {
     float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
     float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
     return (r0 + r1) + (r2 + r3);
-}
-
-// Pairwise tree over N (a power of two) per-lane partials: level by level, p[i] = p[2i] + p[2i+1].
-template <int N>
-__device__ __forceinline__ float tree_sum(float (&p)[N]) {
-#pragma unroll
-    for (int w = N / 2; w >= 1; w /= 2) {
-#pragma unroll
-        for (int i = 0; i < w; ++i) p[i] = p[2 * i] + p[2 * i + 1];
-    }
-    return p[0];
 }
 
 // Sum of squares of eight values in index order.

@@ -23,8 +23,6 @@ struct GatedArgs {
     uint16_t* out;           // bf16 [T, H]
     int64_t T;
     int32_t H;
-    int32_t wpt;
-    int32_t spw;
     float eps;
 };
 
@@ -32,57 +30,43 @@ __device__ __forceinline__ float sigmoid_accurate(float g) {
     return 1.0f / (1.0f + __expf(-g));
 }
 
-template <int VPL>
-__global__ void __launch_bounds__(block_max_for(VPL))
+template <int VPL, int TAIL>
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(VPL == 1 ? 7 : 4, 8)))
 gated_residual_rmsnorm_kernel(const GatedArgs a) {
     extern __shared__ float lds[];
-    const RowMap m = row_map(a.T, a.wpt);
-    if (a.wpt == 1 && !m.valid) return;
-
+    const RowMap m = row_map();
     const int H = a.H;
-    int eoff[VPL];
-    bool sval[VPL];
-#pragma unroll
-    for (int s = 0; s < VPL; ++s) {
-        const int e = (m.wit * a.spw + s) * kSlot + m.lane * kVec;
-        sval[s] = e < H;
-        eoff[s] = sval[s] ? e : 0;
-    }
+    const Slots<VPL, TAIL> sl = slot_offsets<VPL, TAIL>(m, H);
     const int64_t row = m.t * H;
     const uint16_t* xr = a.x + row;
     const uint16_t* gr = a.gate + row;
     const float* res = a.residual + row;
 
+    u32x4 xv[VPL], gv[VPL], gm[VPL];
+    f32x4 rv[VPL][2];
+#pragma unroll
+    for (int s = 0; s < VPL; ++s) {
+        xv[s] = ld_stream(at<u32x4>(xr, sl.eoff[s] * 2u));
+        gv[s] = ld_stream(at<u32x4>(gr, sl.eoff[s] * 2u));
+        rv[s][0] = ld_stream(at<f32x4>(res, sl.eoff[s] * 4u));
+        rv[s][1] = ld_stream(at<f32x4>(res, sl.eoff[s] * 4u + 16u));
+    }
+    load_gamma(gm, a.gamma, sl);
     float r[VPL][8];
 #pragma unroll
     for (int s = 0; s < VPL; ++s) {
-        const u32x4 xv = ld_stream(reinterpret_cast<const u32x4*>(xr + eoff[s]));
-        const u32x4 gv = ld_stream(reinterpret_cast<const u32x4*>(gr + eoff[s]));
-        const f32x4 r0 = ld_stream(reinterpret_cast<const f32x4*>(res + eoff[s]));
-        const f32x4 r1 = ld_stream(reinterpret_cast<const f32x4*>(res + eoff[s] + 4));
         float x[8], g[8];
-        widen8(xv, x);
-        widen8(gv, g);
+        widen8(xv[s], x);
+        widen8(gv[s], g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            r[s][i] = __builtin_fmaf(sigmoid_accurate(g[i]), x[i], r0[i]);
-            r[s][4 + i] = __builtin_fmaf(sigmoid_accurate(g[4 + i]), x[4 + i], r1[i]);
+            r[s][i] = __builtin_fmaf(sigmoid_accurate(g[i]), x[i], rv[s][0][i]);
+            r[s][4 + i] = __builtin_fmaf(sigmoid_accurate(g[4 + i]), x[4 + i], rv[s][1][i]);
         }
     }
-    float* res_out = a.residual_out + row;
-    if (m.valid) {
-#pragma unroll
-        for (int s = 0; s < VPL; ++s) {
-            if (sval[s]) {
-                st_stream(f32x4{r[s][0], r[s][1], r[s][2], r[s][3]},
-                          reinterpret_cast<f32x4*>(res_out + eoff[s]));
-                st_stream(f32x4{r[s][4], r[s][5], r[s][6], r[s][7]},
-                          reinterpret_cast<f32x4*>(res_out + eoff[s] + 4));
-            }
-        }
-    }
-    int parity = 0;
-    rmsnorm_store<VPL>(r, eoff, sval, a.gamma, a.out + row, H, a.eps, lds, parity, m);
+    store_residual(r, sl, a.residual_out + row);
+    TokenLds L = token_lds(lds, m.wpt, 1);
+    rmsnorm_store(r, gm, sl, a.out + row, H, a.eps, L, m);
 }
 
 // ---------------------------------------------------------------------------------------

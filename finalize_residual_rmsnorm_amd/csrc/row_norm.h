@@ -1,15 +1,15 @@
-// Row mapping and the fixed-order row reduction shared by the token-row kernels
-// (MoE finalize and gated-residual RMSNorm).
+// Row mapping and the fixed-order row reduction shared by the token-row kernels (MoE
+// finalize and gated-residual RMSNorm).
 //
-// A token row of H values is cut into slots of 512 values (one 16-byte vector per lane of a
-// wavefront).  A token is handled by `wpt` waves (a power of two); wave w of the token owns
-// the `spw` consecutive slots starting at w * spw, and each lane holds VPL <= spw of them in
-// registers.  Sums over a row always follow one tree, whatever wpt is:
-//   per lane, a pairwise tree over the slot partials (padded to a power of two),
-//   then a pairwise tree over the waves of the token (through LDS),
-//   then the fixed 64-lane order of wave_sum.
-// The launch shape therefore never changes a result bit, which keeps outputs independent of
-// the token count (a different T can pick a different wpt).
+// One workgroup handles one token row of H values.  The row is cut into slots of 512 values
+// (one 16-byte vector per lane of a wavefront, 1 KiB of bf16 or 2 KiB of fp32); the
+// workgroup's `wpt` waves own VPL consecutive slots each: wave w holds slots
+// [w*VPL, w*VPL + VPL), lane l the values [slot*512 + 8l, +8) of each.  The shape depends on H
+// only, never on the token count, so every token is computed the same way whatever the
+// batch: results are bit-identical for a token alone or inside any batch.
+//
+// Sums over the row have one fixed order: per lane, its slots in order; then, per lane
+// position, the waves in order (through LDS); then the fixed 64-lane order of wave_sum.
 #pragma once
 
 #include "mf_device.h"
@@ -17,114 +17,167 @@
 namespace mf {
 
 struct RowMap {
-    int lane;        // lane in the wave
-    int wave;        // wave in the workgroup (uniform)
-    int tok_in_blk;  // token slot within the workgroup (uniform)
-    int wit;         // wave index within the token (uniform)
-    int wpt;         // waves per token
-    int64_t t;       // token (clamped to T-1 for the spare waves of the last workgroup)
-    bool valid;      // false for spare waves: they compute but store nothing
+    int lane;   // lane in the wave
+    int wave;   // wave in the workgroup = wave in the token (uniform)
+    int wpt;    // waves per token = waves per workgroup
+    int64_t t;  // token
 };
 
-__device__ __forceinline__ RowMap row_map(int64_t T, int wpt) {
+__device__ __forceinline__ RowMap row_map() {
     RowMap m;
     m.lane = threadIdx.x & (kWave - 1);
     m.wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    m.wpt = wpt;
-    m.tok_in_blk = m.wave / wpt;
-    m.wit = m.wave - m.tok_in_blk * wpt;
-    const int tpb = (int)(blockDim.x / kWave) / wpt;
-    int64_t t = (int64_t)blockIdx.x * tpb + m.tok_in_blk;
-    m.valid = t < T;
-    m.t = m.valid ? t : T - 1;
+    m.wpt = blockDim.x / kWave;
+    m.t = blockIdx.x;
     return m;
 }
 
-// Reduce NR row sums.  On entry v[n] is this lane's tree root over its slots; on exit every
-// lane of every wave of the token holds the token total.  With wpt > 1 the waves of a token
-// meet at workgroup barriers, so every wave of the workgroup must make the same calls.
-// Layout of `lds` (floats): two halves, each [waves per workgroup][NR][64] lane partials
-// followed by [waves per workgroup][NR] totals; `parity` alternates the halves so that no
-// extra barrier is needed before a half is reused.
-//  - NR == 1: one barrier; every wave combines the wpt partials of its lane itself.
-//  - NR > 1: wave w of the token finishes rows w, w + wpt, ... and publishes the totals;
-//    a second barrier, then every wave reads the NR totals.  This keeps the registers at
-//    WPT_MAX per row instead of NR * WPT_MAX.
-template <int NR, int WPT_MAX>
-__device__ __forceinline__ void token_sum(float (&v)[NR], float* lds, int& parity,
-                                          const RowMap& m) {
-    if (m.wpt > 1) {
-        const int nw = blockDim.x / kWave;
-        float* part = lds + (size_t)parity * nw * NR * (kWave + 1);
-        float* tot = part + nw * NR * kWave;
+// How a row's slots meet its end:
+//   kRowFull   - H = wpt * VPL * 512: every slot of every wave is inside the row;
+//   kRowWhole  - H is a multiple of 512: a slot is entirely inside or entirely past the row,
+//                so validity is uniform per wave and slot;
+//   kRowRagged - the last slot is cut inside, so validity is per lane.
+enum RowTail { kRowFull = 0, kRowWhole = 1, kRowRagged = 2 };
+
+// Offsets of the slots a lane holds.  eoff[s]: element offset of its 8 values (0 when they
+// lie past H); sval[s]: they lie inside the row; suni[s] (wave-uniform): the slot starts
+// inside the row.
+template <int VPL, int TAIL>
+struct Slots {
+    uint32_t eoff[VPL];
+    bool sval[VPL];
+    bool suni[VPL];
+};
+
+template <int VPL, int TAIL>
+__device__ __forceinline__ Slots<VPL, TAIL> slot_offsets(const RowMap& m, int H) {
+    Slots<VPL, TAIL> sl;
 #pragma unroll
-        for (int n = 0; n < NR; ++n) part[(m.wave * NR + n) * kWave + m.lane] = v[n];
-        __syncthreads();
-        const int base = m.tok_in_blk * m.wpt;
-        parity ^= 1;
-        if constexpr (NR == 1) {
-            float c[WPT_MAX];
+    for (int s = 0; s < VPL; ++s) {
+        const int slot = m.wave * VPL + s;
+        const uint32_t e = uint32_t(slot * kSlot + m.lane * kVec);
+        sl.suni[s] = TAIL == kRowFull || slot * kSlot < H;
+        sl.sval[s] = TAIL == kRowRagged ? e < uint32_t(H) : sl.suni[s];
+        sl.eoff[s] = sl.sval[s] ? e : 0u;
+    }
+    return sl;
+}
+
+// Cross-wave reductions of a token go through LDS in two alternating halves, each sized
+// for the largest number of sums (NRMAX) any call of the kernel reduces at once: a half holds
+// [wpt][NR][64] lane partials followed by [NR] totals.  Consecutive calls use different
+// halves, and a half is only rewritten two calls later, after every wave has passed the
+// barrier of the call in between, i.e. after every wave has finished reading it.
+struct TokenLds {
+    float* base;
+    int half;    // floats per half
+    int parity;  // half the next call uses
+};
+
+__device__ __forceinline__ TokenLds token_lds(float* lds, int wpt, int nr_max) {
+    return TokenLds{lds, wpt * nr_max * kWave + nr_max, 0};
+}
+
+// Reduce NR row sums over the token (NR <= the NRMAX the LDS was sized for).  On entry v[n]
+// is this lane's partial; on exit every lane of every wave holds the token total.  With
+// wpt > 1 the waves meet at workgroup barriers, so all waves must make the same calls.
+//  - NR == 1: one barrier; every wave adds the wpt partials of its lane position in order.
+//  - NR > 1: wave w finishes rows w, w + wpt, ... and publishes them; a second barrier, then
+//    every wave reads the NR totals.
+// Sum, in wave order, of the wpt partials held at part[w * stride + lane] (all reads issued
+// together; trailing zeros for w >= wpt leave the sum unchanged: a sum of squares is never -0).
+__device__ __forceinline__ float sum_waves(const float* part, int stride, int wpt, int lane) {
+    constexpr int kMaxWaves = 16;
+    float c[kMaxWaves];
 #pragma unroll
-            for (int w = 0; w < WPT_MAX; ++w)
-                c[w] = (w < m.wpt) ? part[(base + w) * kWave + m.lane] : 0.0f;
-            v[0] = wave_sum(tree_sum<WPT_MAX>(c));
-        } else {
-            for (int n = m.wit; n < NR; n += m.wpt) {
-                float c[WPT_MAX];
+    for (int w = 0; w < kMaxWaves; ++w) c[w] = w < wpt ? part[w * stride + lane] : 0.0f;
+    float s = c[0];
 #pragma unroll
-                for (int w = 0; w < WPT_MAX; ++w)
-                    c[w] = (w < m.wpt) ? part[((base + w) * NR + n) * kWave + m.lane] : 0.0f;
-                const float q = wave_sum(tree_sum<WPT_MAX>(c));
-                if (m.lane == 0) tot[m.tok_in_blk * NR + n] = q;
-            }
-            __syncthreads();
+    for (int w = 1; w < kMaxWaves; ++w) s += c[w];
+    return s;
+}
+
+template <int NR>
+__device__ __forceinline__ void token_sum(float (&v)[NR], TokenLds& L, const RowMap& m) {
+    if (m.wpt == 1) {
 #pragma unroll
-            for (int n = 0; n < NR; ++n) v[n] = tot[m.tok_in_blk * NR + n];
-        }
+        for (int n = 0; n < NR; ++n) v[n] = wave_sum(v[n]);
         return;
     }
+    float* part = L.base + (size_t)L.parity * L.half;
+    float* tot = part + m.wpt * NR * kWave;
+    L.parity ^= 1;
 #pragma unroll
-    for (int n = 0; n < NR; ++n) v[n] = wave_sum(v[n]);
+    for (int n = 0; n < NR; ++n) part[(m.wave * NR + n) * kWave + m.lane] = v[n];
+    __syncthreads();
+    if constexpr (NR == 1) {
+        v[0] = wave_sum(sum_waves(part, kWave, m.wpt, m.lane));
+    } else {
+        for (int n = m.wave; n < NR; n += m.wpt) {
+            const float s = wave_sum(sum_waves(part + n * kWave, NR * kWave, m.wpt, m.lane));
+            if (m.lane == 0) tot[n] = s;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < NR; ++n) v[n] = tot[n];
+    }
 }
 
-// LDS bytes token_sum needs for a workgroup of `waves` waves reducing NR sums per call.
-constexpr size_t token_sum_lds_bytes(int waves, int nr) {
-    return size_t(2) * waves * nr * (kWave + 1) * sizeof(float);
+// LDS bytes for `wpt` waves reducing at most nr_max sums per call.
+constexpr size_t token_sum_lds_bytes(int wpt, int nr_max) {
+    return wpt > 1 ? size_t(2) * (wpt * nr_max * kWave + nr_max) * sizeof(float) : 0;
 }
 
-// Largest waves-per-token a VPL instantiation is launched with, and the matching workgroup
-// bound: the row slice in registers shrinks as the token is spread over more waves.
-constexpr int wpt_max_for(int vpl) { return vpl <= 4 ? 16 : (vpl <= 8 ? 8 : 4); }
-constexpr int block_max_for(int vpl) { return vpl <= 4 ? 1024 : (vpl <= 8 ? 512 : 256); }
+// Sum of squares of the lane's valid values, its slots in order.
+template <int VPL, int TAIL>
+__device__ __forceinline__ float lane_sumsq(const float (&r)[VPL][8], const Slots<VPL, TAIL>& sl) {
+    float p = 0.0f;
+#pragma unroll
+    for (int s = 0; s < VPL; ++s) p += sl.sval[s] ? sumsq8(r[s]) : 0.0f;
+    return p;
+}
+
+// Store of the updated fp32 residual row (after every residual load of the row).
+template <int VPL, int TAIL>
+__device__ __forceinline__ void store_residual(const float (&r)[VPL][8],
+                                               const Slots<VPL, TAIL>& sl, float* row) {
+#pragma unroll
+    for (int s = 0; s < VPL; ++s) {
+        if (sl.sval[s]) {
+            st_stream(f32x4{r[s][0], r[s][1], r[s][2], r[s][3]}, at<f32x4>(row, sl.eoff[s] * 4u));
+            st_stream(f32x4{r[s][4], r[s][5], r[s][6], r[s][7]},
+                      at<f32x4>(row, sl.eoff[s] * 4u + 16u));
+        }
+    }
+}
+
+// gamma slice of the lane (bf16, loaded early so that its latency overlaps other work).
+template <int VPL, int TAIL>
+__device__ __forceinline__ void load_gamma(u32x4 (&g)[VPL], const uint16_t* gamma,
+                                           const Slots<VPL, TAIL>& sl) {
+#pragma unroll
+    for (int s = 0; s < VPL; ++s) g[s] = *at<u32x4>(gamma, sl.eoff[s] * 2u);
+}
 
 // Final RMSNorm of a row held as r[VPL][8] (fp32) and the bf16 store of out:
 //   out = bf16((r * (sum(r^2)/H + eps)^-1/2) * gamma).
-// `eoff[s]` is the element offset of slot s (0 for slots past H), `sval[s]` its validity.
-template <int VPL>
-__device__ __forceinline__ void rmsnorm_store(float (&r)[VPL][8], const int (&eoff)[VPL],
-                                              const bool (&sval)[VPL], const uint16_t* gamma,
-                                              uint16_t* out_row, int H, float eps, float* lds,
-                                              int& parity, const RowMap& m) {
-    constexpr int NP = next_pow2(VPL);
-    float p[NP];
-#pragma unroll
-    for (int s = 0; s < NP; ++s) p[s] = 0.0f;
-#pragma unroll
-    for (int s = 0; s < VPL; ++s) p[s] = sval[s] ? sumsq8(r[s]) : 0.0f;
-    float ss[1] = {tree_sum<NP>(p)};
-    token_sum<1, wpt_max_for(VPL)>(ss, lds, parity, m);
+template <int VPL, int TAIL>
+__device__ __forceinline__ void rmsnorm_store(const float (&r)[VPL][8], const u32x4 (&g)[VPL],
+                                              const Slots<VPL, TAIL>& sl, uint16_t* out_row,
+                                              int H, float eps, TokenLds& L, const RowMap& m) {
+    float ss[1] = {lane_sumsq(r, sl)};
+    token_sum<1>(ss, L, m);
     const float inv = 1.0f / __builtin_sqrtf(ss[0] / (float)H + eps);
 #pragma unroll
     for (int s = 0; s < VPL; ++s) {
-        const u32x4 g = *reinterpret_cast<const u32x4*>(gamma + eoff[s]);
         float gf[8];
-        widen8(g, gf);
+        widen8(g[s], gf);
         u32x4 o;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             o[i] = pack_bf16x2((r[s][2 * i] * inv) * gf[2 * i],
                                (r[s][2 * i + 1] * inv) * gf[2 * i + 1]);
-        if (m.valid && sval[s]) st_stream(o, reinterpret_cast<u32x4*>(out_row + eoff[s]));
+        if (sl.sval[s]) st_stream(o, at<u32x4>(out_row, sl.eoff[s] * 2u));
     }
 }
 

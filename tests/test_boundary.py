@@ -73,7 +73,7 @@ def fin(rows=A, num_rows=32, idx=B, w=C, eids=None, eg=None, E=0, res=D, res_out
     (dict(out=G + 2), ALIGN), (dict(idx=B + 2), ALIGN), (dict(gamma=F + 8), ALIGN),
     (dict(res_out=D + 64), ALIAS), (dict(out=A + 1024), ALIAS), (dict(out=E_ + 4096), ALIAS),
     (dict(res_out=B), ALIAS), (dict(out=F), ALIAS),
-    (dict(T=1 << 27), SHAPE),  # 64 lanes per token would overflow the 32-bit grid
+    (dict(T=1 << 26), SHAPE),  # 128 threads per token would overflow the 32-bit grid
 ])
 def test_finalize_rejects_bad_arguments(kw, code):
     assert fin(**kw) == code
@@ -131,20 +131,40 @@ def test_stream_copy_rejects_bad_arguments():
 
 
 def test_launch_shapes():
-    # prefill: a wave per token row, 14 slots of 512 values per lane, 4 tokens per workgroup
+    # One workgroup per token; its waves (a power of two, at most 16) hold slots of 512
+    # values.  The shape depends on H only, never on the token count.
+    # prefill: 14 slots over 16 waves (two spare waves skip their loads)
     assert mf.mf_launch_shape(mf.KIND_FINALIZE, 16384, 7168, 8) == dict(
-        waves_per_token=1, vectors_per_lane=14, block=256, grid=4096)
-    # decode with per-expert norm: the row is spread over 8 waves
+        waves_per_token=16, vectors_per_lane=1, block=1024, grid=16384)
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 3, 7168, 8) == dict(
+        waves_per_token=16, vectors_per_lane=1, block=1024, grid=3)
+    # decode with per-expert norm: 8 waves
     assert mf.mf_launch_shape(mf.KIND_FINALIZE_PER_EXPERT, 64, 4096, 8) == dict(
         waves_per_token=8, vectors_per_lane=1, block=512, grid=64)
-    # tiny: H = 1024 is two slots, one per wave
+    # tiny: H = 1024 is two slots
     assert mf.mf_launch_shape(mf.KIND_FINALIZE, 16, 1024, 2) == dict(
-        waves_per_token=2, vectors_per_lane=1, block=256, grid=8)
-    assert mf.mf_launch_shape(mf.KIND_GATED, 4096, 8192)["vectors_per_lane"] == 16
-    # the widest row needs 4 waves of 16 slots
-    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 100000, 32768, 8)["waves_per_token"] == 4
+        waves_per_token=2, vectors_per_lane=1, block=128, grid=16)
+    assert mf.mf_launch_shape(mf.KIND_GATED, 4096, 8192) == dict(
+        waves_per_token=16, vectors_per_lane=1, block=1024, grid=4096)
+    # 12288 = 24 slots: 8 waves of 3 leave no spare slot (16 waves of 2 would leave 8)
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 5, 12288, 8) == dict(
+        waves_per_token=8, vectors_per_lane=3, block=512, grid=5)
+    # the widest row: 64 slots over 16 waves
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 100000, 32768, 8)["vectors_per_lane"] == 4
     with pytest.raises(mf.MFError):
         mf.mf_launch_shape(mf.KIND_FINALIZE, 4, 1001, 2)
+
+
+def test_every_supported_width_has_a_kernel():
+    # The launch-shape query runs the same kernel lookup as a launch: every width and top-k
+    # the capability queries accept must map to a compiled kernel.
+    for H in range(8, 32768 + 1, 8):
+        for kind, k in ((mf.KIND_FINALIZE, 8), (mf.KIND_FINALIZE, 3),
+                        (mf.KIND_FINALIZE_PER_EXPERT, 8), (mf.KIND_FINALIZE_PER_EXPERT, 5),
+                        (mf.KIND_GATED, 1)):
+            s = mf.mf_launch_shape(kind, 1000, H, k)
+            assert s["waves_per_token"] * s["vectors_per_lane"] * 512 >= H, (kind, H, k)
+            assert s["block"] <= (512 if kind == mf.KIND_FINALIZE_PER_EXPERT else 1024)
 
 
 def test_binding_refuses_cpu_tensors():
