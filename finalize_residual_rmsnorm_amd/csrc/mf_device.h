@@ -47,7 +47,7 @@ __device__ __forceinline__ T* at(void* base, uint32_t byte_off) {
     return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + byte_off);
 }
 
-// Single-use streams (gathered rows, residual in/out, outputs) bypass cache retention.
+// Single-use streams (gathered rows, residual in/out) bypass cache retention.
 template <class T>
 __device__ __forceinline__ T ld_stream(const T* p) { return __builtin_nontemporal_load(p); }
 template <class T>
