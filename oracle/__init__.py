@@ -1,4 +1,5 @@
-"""CPU oracle for the MoE finalize path and the two sibling fused norms.
+"""CPU oracle for the MoE finalize path, the two sibling fused norms, and the routing and
+expert-sorted permutation the finalize consumes.
 
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg
 of ``bench.py`` are the only callers.  The product path never imports this package, and
@@ -44,6 +45,7 @@ def _load():
         lib.oracle_moe_finalize.argtypes = [p, i64, p, p, p, p, i32, p, p, p, f32, p, i64, i32, i32]
         lib.oracle_gated_residual_rmsnorm.argtypes = [p, p, p, p, p, f32, p, i64, i32]
         lib.oracle_rmsnorm_sigmoid_gate.argtypes = [p, p, p, f32, p, i64, i32, i32]
+        lib.oracle_moe_route.argtypes = [p, i64, i32, i32, p, p, p, p, p]
         lib.oracle_bf16_round.argtypes = [p, p, i64]
         lib.oracle_bf16_round.restype = None
         _lib = lib
@@ -115,6 +117,29 @@ def rmsnorm_sigmoid_gate(x, gate, gamma, eps):
     lib.oracle_rmsnorm_sigmoid_gate(px, pgt, pg, float(eps), out.ctypes.data_as(ctypes.c_void_p),
                                     T, heads, D)
     return out
+
+
+def moe_route(logits, k):
+    """Top-k softmax routing and the expert-sorted permutation of float32 logits [T, E].
+
+    Returns (expert_ids int32 [T,k], weights float32 [T,k], idx int32 [T,k],
+    perm int32 [T*k], offsets int32 [E+1]).
+    """
+    lib = _load()
+    lg, plg = _c(logits, np.float32)
+    T, E = lg.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    eids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    idx = np.empty((T, k), np.int32)
+    perm = np.empty(T * k, np.int32)
+    off = np.empty(E + 1, np.int32)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    st = lib.oracle_moe_route(plg, T, E, k, ptr(eids), ptr(w), ptr(idx), ptr(perm), ptr(off))
+    if st != 0:
+        raise ValueError(f"oracle_moe_route failed with status {st}")
+    return eids, w, idx, perm, off
 
 
 def bf16_round(v):

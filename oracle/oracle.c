@@ -190,3 +190,70 @@ int oracle_rmsnorm_sigmoid_gate(const uint16_t* x, const uint16_t* gate, const u
 void oracle_bf16_round(const double* v, uint16_t* out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = bf16_round(v[i]);
 }
+
+/*
+ * MoE routing and the expert-sorted permutation: the inputs the finalize consumes.
+ *
+ * Per token t (logits[t, 0..E-1]):
+ *   expert_ids[t, j], j = 0..k-1: the experts of the k largest logits, largest first; equal
+ *     logits go to the lower expert id;
+ *   weights[t, j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected logits (a
+ *     softmax over the top k), in float64, rounded once to float32.
+ * Over all slots s = t*k + j (the flattened order), a stable sort by expert id gives the
+ * contiguous grouped-GEMM layout (page "FlashInfer: fused kernels and an optimised scheduler
+ * for MoE", PR #4130, the m_indptr / token_offset arguments of its grouped GEMM):
+ *   offsets[e] = number of slots routed to experts < e, offsets[E] = T*k;
+ *   perm[p] = the slot stored at permuted row p (rows grouped by expert, slots ascending);
+ *   idx[s] = the permuted row of slot s, so idx[perm[p]] = p.
+ * Returns 0, or -2 if scratch memory cannot be allocated.
+ */
+int oracle_moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* expert_ids,
+                     float* weights, int32_t* idx, int32_t* perm, int32_t* offsets) {
+    unsigned char* taken = (unsigned char*)malloc((size_t)(E > 0 ? E : 1));
+    int64_t* cursor = (int64_t*)malloc(sizeof(int64_t) * (size_t)(E > 0 ? E : 1));
+    double* ex = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+    if (!taken || !cursor || !ex) {
+        free(taken);
+        free(cursor);
+        free(ex);
+        return -2;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        const float* l = logits + t * (int64_t)E;
+        for (int32_t e = 0; e < E; ++e) taken[e] = 0;
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < E; ++e)
+                if (!taken[e] && (best < 0 || l[e] > l[best])) best = e;  /* ties keep the lower id */
+            taken[best] = 1;
+            expert_ids[t * k + j] = best;
+        }
+        double top = (double)l[expert_ids[t * k]];
+        double sum = 0.0;
+        for (int32_t j = 0; j < k; ++j) {
+            ex[j] = exp((double)l[expert_ids[t * k + j]] - top);
+            sum += ex[j];
+        }
+        for (int32_t j = 0; j < k; ++j) weights[t * k + j] = (float)(ex[j] / sum);
+    }
+    /* counting sort of the slots by expert id, stable in slot order */
+    for (int32_t e = 0; e < E; ++e) cursor[e] = 0;
+    for (int64_t s = 0; s < T * k; ++s) cursor[expert_ids[s]] += 1;
+    int64_t run = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        int64_t c = cursor[e];
+        offsets[e] = (int32_t)run;
+        cursor[e] = run;
+        run += c;
+    }
+    offsets[E] = (int32_t)run;
+    for (int64_t s = 0; s < T * k; ++s) {
+        int64_t p = cursor[expert_ids[s]]++;
+        idx[s] = (int32_t)p;
+        perm[p] = (int32_t)s;
+    }
+    free(taken);
+    free(cursor);
+    free(ex);
+    return 0;
+}

@@ -368,3 +368,62 @@ def test_per_head_heads_are_independent():
     p = np.array([3, 0, 4, 1, 2])
     o2 = oracle.rmsnorm_sigmoid_gate(d["x"][:, p], d["gate"][:, p], d["gamma"], d["eps"])
     assert np.array_equal(o[:, p], o2)
+
+
+# ----------------------------------------------------------------------------- routing
+
+
+def test_golden_route_hand_example():
+    g = json.load(open(GOLDEN))["moe_route"]
+    eids, w, idx, perm, off = oracle.moe_route(np.array(g["logits"], np.float32), g["k"])
+    assert eids.tolist() == g["expected_expert_ids"]
+    assert w.tolist() == g["expected_weights"]
+    assert idx.tolist() == g["expected_idx"]
+    assert perm.tolist() == g["expected_perm"]
+    assert off.tolist() == g["expected_offsets"]
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 4, 1), (5, 8, 2), (33, 64, 8), (100, 256, 8), (7, 130, 16),
+                                   (3, 16, 16)])
+def test_route_matches_numpy_sorts_and_scipy_softmax(T, E, k):
+    rng = np.random.default_rng(300 + T + E + k)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, ::5] = np.round(logits[:, ::5])  # plenty of exact ties
+    eids, w, idx, perm, off = oracle.moe_route(logits, k)
+    want = np.argsort(-logits, axis=1, kind="stable")[:, :k]     # ties: lower id first
+    assert np.array_equal(eids, want)
+    from scipy.special import softmax
+    top = np.take_along_axis(logits, want, axis=1).astype(np.float64)
+    ref = softmax(top, axis=1).astype(np.float32)
+    assert np.all(np.abs(w.astype(np.float64) - ref) <= np.spacing(ref) * 1.0001)
+    assert np.array_equal(perm, np.argsort(eids.ravel(), kind="stable"))
+    assert np.array_equal(idx.ravel()[perm], np.arange(T * k))
+    assert np.array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(eids.ravel(), minlength=E))]))
+
+
+def test_route_k_equals_e_is_a_full_softmax():
+    rng = np.random.default_rng(310)
+    logits = rng.standard_normal((6, 12)).astype(np.float32)
+    eids, w, _, _, off = oracle.moe_route(logits, 12)
+    assert np.array_equal(np.sort(eids, axis=1), np.tile(np.arange(12), (6, 1)))
+    full = np.exp(logits.astype(np.float64) - logits.max(axis=1, keepdims=True))
+    full /= full.sum(axis=1, keepdims=True)
+    assert np.allclose(w, np.take_along_axis(full, eids, axis=1), rtol=2e-7, atol=0)
+    assert np.array_equal(off, np.arange(13) * 6)
+
+
+def test_route_matches_the_input_generator_layout():
+    # The seeded generator draws the same routing in float64 with numpy; on logits that are
+    # exact in float32 the selection and the expert-sorted layout must agree exactly.
+    rng = np.random.default_rng(311)
+    logits = rng.standard_normal((50, 32)).astype(np.float32)
+
+    class Fixed:
+        @staticmethod
+        def standard_normal(shape):
+            return logits.astype(np.float64)
+    ids, w = workloads.topk_softmax_routing(Fixed(), 50, 32, 4)
+    eids, w_o, idx, perm, off = oracle.moe_route(logits, 4)
+    assert np.array_equal(eids, ids)
+    assert np.allclose(w_o, w, rtol=1e-6, atol=0)
+    assert np.array_equal(idx, workloads.unpermute_index(None, ids, "expert_sorted"))
