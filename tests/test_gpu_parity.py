@@ -111,10 +111,10 @@ def test_finalize_tiny_workload():
 
 FINALIZE_SHAPES = [
     (1, 8, 1, "random"), (3, 24, 2, "random"), (5, 520, 3, "random"),
-    (17, 1024, 8, "expert_sorted"), (33, 4104, 9, "random"), (100, 7168, 8, "expert_sorted"),
-    (2049, 7168, 8, "expert_sorted"), (7, 8192, 16, "random"), (5, 12288, 4, "random"),
-    (3000, 12288, 2, "expert_sorted"), (4, 32768, 3, "random"), (2100, 32768, 1, "random"),
-    (4097, 2048, 5, "expert_sorted"), (6, 3584, 64, "random"),
+    (17, 1024, 8, "expert_grouped"), (33, 4104, 9, "random"), (100, 7168, 8, "expert_grouped"),
+    (2049, 7168, 8, "expert_grouped"), (7, 8192, 16, "random"), (5, 12288, 4, "random"),
+    (3000, 12288, 2, "expert_grouped"), (4, 32768, 3, "random"), (2100, 32768, 1, "random"),
+    (4097, 2048, 5, "expert_grouped"), (6, 3584, 64, "random"),
 ]
 
 

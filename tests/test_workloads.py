@@ -15,43 +15,43 @@ def test_same_seed_same_bytes():
     assert not np.array_equal(a["expert_rows"], c["expert_rows"])
 
 
-@pytest.mark.parametrize("layout", ["random", "expert_sorted"])
+@pytest.mark.parametrize("layout", ["random", "expert_grouped"])
 def test_idx_is_a_bijection(layout):
     d = workloads.make_finalize_inputs(37, 16, E=12, k=5, seed=3, layout=layout)
     assert d["idx"].dtype == np.int32 and d["idx"].shape == (37, 5)
     assert np.array_equal(np.sort(d["idx"].ravel()), np.arange(37 * 5))
 
 
-def test_expert_sorted_rows_are_grouped_by_expert():
-    d = workloads.make_finalize_inputs(64, 16, E=32, k=8, seed=4, layout="expert_sorted")
+def test_expert_grouped_rows_are_grouped_by_expert():
+    d = workloads.make_finalize_inputs(64, 16, E=32, k=8, seed=4, layout="expert_grouped")
     n = 64 * 8
     expert_of_row = np.empty(n, np.int64)
     expert_of_row[d["idx"].ravel()] = d["expert_ids"].ravel()
     assert np.all(np.diff(expert_of_row) >= 0)
-    # stable: within one expert, rows follow the flattened (t, j) slot order
-    slot_of_row = np.empty(n, np.int64)
-    slot_of_row[d["idx"].ravel()] = np.arange(n)
-    same = np.diff(expert_of_row) == 0
-    assert np.all(np.diff(slot_of_row)[same] > 0)
 
 
-def test_routing_weights_are_a_topk_softmax():
+def test_routing_draw_is_distinct_experts_and_simplex_weights():
     d = workloads.make_finalize_inputs(50, 8, E=16, k=4, seed=5)
     w = d["weights"].astype(np.float64)
     assert np.allclose(w.sum(axis=1), 1.0, atol=1e-6)
-    assert np.all(np.diff(w, axis=1) <= 0)          # descending logit order
-    for t in range(50):                              # distinct experts per token
+    assert np.all(w > 0) and np.all(np.diff(w, axis=1) <= 0)   # largest first
+    for t in range(50):                                           # distinct experts per token
         assert len(set(d["expert_ids"][t])) == 4
     assert d["expert_ids"].min() >= 0 and d["expert_ids"].max() < 16
+    # k == E: every expert once per token
+    d = workloads.make_finalize_inputs(6, 8, E=5, k=5, seed=6)
+    assert np.array_equal(np.sort(d["expert_ids"], axis=1), np.tile(np.arange(5), (6, 1)))
 
 
-def test_topk_ties_go_to_lower_expert_id():
-    class Flat:  # a stand-in rng whose logits are all equal
-        @staticmethod
-        def standard_normal(shape):
-            return np.zeros(shape)
-    ids, w = workloads.topk_softmax_routing(Flat(), 3, 6, 2)
-    assert np.array_equal(ids, [[0, 1]] * 3) and np.allclose(w, 0.5)
+def test_route_inputs():
+    d = workloads.make_inputs("moe_route_prefill", T=32)
+    assert d["logits"].shape == (32, 256) and d["logits"].dtype == np.float32
+    assert abs(d["logits"].std() - 1.0) < 0.05
+    q = workloads.make_inputs("moe_route_decode")
+    assert q["logits"].shape == (64, 128) and q["k"] == 8
+    # bf16-valued: the low 16 bits are zero, and equal logits occur
+    assert np.all(q["logits"].view(np.uint32) & 0xFFFF == 0)
+    assert any(len(set(r.tolist())) < len(r) for r in q["logits"])
 
 
 def test_shapes_and_dtypes_of_named_workloads():

@@ -1,27 +1,33 @@
-"""Seeded synthetic inputs for the MoE finalize path and its two sibling fused norms.
+"""Seeded synthetic inputs for the MoE finalize path, its two sibling fused norms and the
+routing that feeds the finalize.
 
 This module only draws random inputs.  It holds none of the arithmetic the path computes:
-no gather, no accumulation, no normalisation and no output rounding.  The oracle, the GPU
-tests, ``bench.py`` and ``__graft_entry__.smoke()`` all take their inputs from here, so both
-sides of every parity check see the same bytes.
+no top-k selection or softmax, no stable permutation, no gather, no accumulation, no
+normalisation and no output rounding.  The finalize's routing inputs are drawn directly
+(random distinct experts, random weights, a random expert-grouped row order), not computed
+from logits.  The oracle, the GPU tests, ``bench.py`` and ``__graft_entry__.smoke()`` all take
+their inputs from here, so both sides of every parity check see the same bytes.
 
 Recipe (numpy ``default_rng(seed)``, PCG64; draws happen in the order listed):
 
 * MoE finalize (``make_finalize_inputs``):
-    1. routing logits ``[T, E]`` ~ N(0, 1) in float64;
-    2. the top-k experts per token: a stable argsort of the negated logits, so the k
-       largest logits come first, in descending order, and ties go to the lower expert id;
-    3. routing weights: a softmax over those k logits, in float64, cast to float32;
-    4. the unpermute index ``idx [T, k]`` (int32): the permuted GEMM2 output row that holds
+    1. expert ids ``[T, k]`` (int32): k distinct experts per token, uniformly at random (the
+       first k entries of an independent random permutation of the E experts per token);
+    2. routing weights ``[T, k]`` (float32): k Exp(1) draws per token divided by their sum
+       (a uniform draw from the probability simplex), listed largest first;
+    3. the unpermute index ``idx [T, k]`` (int32): the permuted GEMM2 output row that holds
        the output of slot (t, j):
          - ``layout="random"``: ``rng.permutation(T*k)``;
-         - ``layout="expert_sorted"``: a stable sort of the flattened (t, j) slots by expert
-           id, which is the contiguous grouped-GEMM layout (rows grouped by expert);
-    5. expert rows ``[T*k, H]`` ~ N(0, 1), drawn as float32 in chunks of 2**24 values and
+         - ``layout="expert_grouped"``: rows grouped by expert id in ascending expert order
+           (the grouped-GEMM layout), in a random order within each expert;
+    4. expert rows ``[T*k, H]`` ~ N(0, 1), drawn as float32 in chunks of 2**24 values and
        rounded to bfloat16 (round-to-nearest-even, by torch's CPU cast);
-    6. residual ``[T, H]`` float32 ~ N(0, residual_std);
-    7. gamma ``[H]`` = 1 + 0.1 * N(0, 1), rounded to bfloat16;
-    8. (per-expert variant only) expert gammas ``[E, H]`` = 1 + 0.1 * N(0, 1), bfloat16.
+    5. residual ``[T, H]`` float32 ~ N(0, residual_std);
+    6. gamma ``[H]`` = 1 + 0.1 * N(0, 1), rounded to bfloat16;
+    7. (per-expert variant only) expert gammas ``[E, H]`` = 1 + 0.1 * N(0, 1), bfloat16.
+* MoE routing (``make_route_inputs``): router logits ``[T, E]`` ~ N(0, 1) float32, optionally
+  rounded to bfloat16 values (``bf16_logits``: the precision of a bf16 router GEMM, which
+  makes exactly equal logits common).
 * Gated-residual RMSNorm (``make_gated_inputs``): x ``[T, H]`` ~ N(0, 1) bf16,
   gate ``[T, H]`` ~ N(0, 2) bf16 (standard deviation 2), residual ``[T, H]`` ~ N(0, 1) fp32,
   gamma ``[H]`` = 1 + 0.1 * N(0, 1) bf16.
@@ -37,7 +43,7 @@ import torch
 
 CHUNK = 1 << 24  # values per draw when filling large arrays
 
-#: The five named workloads, with the sizes the MoE finalize pages and their model
+#: The named workloads, with the sizes the MoE finalize pages and their model
 #: configurations work at.  ``seed`` fixes every draw.
 WORKLOADS = {
     # Tiny finalize: correctness-sized, random permutation.
@@ -46,15 +52,19 @@ WORKLOADS = {
     # Decode-sized finalize with a per-expert RMSNorm on every gathered row
     # (tensor-parallel finalize at hidden 4096, top-k 8).
     "finalize_decode_per_expert": dict(kind="finalize", T=64, H=4096, E=128, k=8, seed=2,
-                                       layout="expert_sorted", per_expert=True,
+                                       layout="expert_grouped", per_expert=True,
                                        residual_std=2.0),
     # Prefill-sized deterministic finalize: the throughput workload.
     "finalize_prefill": dict(kind="finalize", T=16384, H=7168, E=256, k=8, seed=3,
-                             layout="expert_sorted", per_expert=False, residual_std=1.0),
+                             layout="expert_grouped", per_expert=False, residual_std=1.0),
     # Gated-residual RMSNorm at its fixed hidden size.
     "gated_residual_rmsnorm": dict(kind="gated", T=4096, H=8192, seed=4),
     # Per-head RMSNorm + sigmoid gate at its fixed head dim.
     "rmsnorm_sigmoid_gate": dict(kind="per_head", T=4096, heads=64, D=64, seed=5),
+    # Routing that produces the prefill finalize's gather indices and weights.
+    "moe_route_prefill": dict(kind="route", T=16384, E=256, k=8, seed=6, bf16_logits=False),
+    # Decode-sized routing with bf16-valued logits (frequent exact ties).
+    "moe_route_decode": dict(kind="route", T=64, E=128, k=8, seed=7, bf16_logits=True),
 }
 
 EPS = 1e-6
@@ -94,20 +104,19 @@ def _normal_bf16(rng: np.random.Generator, n: int, std: float = 1.0) -> np.ndarr
     return out
 
 
-def topk_softmax_routing(rng: np.random.Generator, T: int, E: int, k: int):
-    """Top-k routing from N(0,1) logits: (expert_ids [T,k] int32, weights [T,k] float32).
+def draw_routing(rng: np.random.Generator, T: int, E: int, k: int):
+    """Random routing decisions: (expert_ids [T,k] int32, weights [T,k] float32).
 
-    Experts are listed by descending logit (ties to the lower id); the weights are a
-    softmax over the k selected logits.
+    k distinct experts per token, uniformly at random; weights uniform on the simplex
+    (normalised Exp(1) draws), largest first.
     """
     if not 1 <= k <= E:
         raise ValueError(f"need 1 <= k <= E, got k={k}, E={E}")
-    logits = rng.standard_normal((T, E))
-    order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
-    top = np.take_along_axis(logits, order, axis=1)
-    z = np.exp(top - top[:, :1])
-    w = z / z.sum(axis=1, keepdims=True)
-    return order.astype(np.int32), w.astype(np.float32)
+    experts = np.tile(np.arange(E, dtype=np.int32), (T, 1))
+    expert_ids = np.ascontiguousarray(rng.permuted(experts, axis=1)[:, :k])
+    z = rng.exponential(size=(T, k))
+    w = -np.sort(-(z / z.sum(axis=1, keepdims=True)), axis=1)
+    return expert_ids, w.astype(np.float32)
 
 
 def unpermute_index(rng: np.random.Generator, expert_ids: np.ndarray, layout: str) -> np.ndarray:
@@ -116,19 +125,19 @@ def unpermute_index(rng: np.random.Generator, expert_ids: np.ndarray, layout: st
     n = T * k
     if layout == "random":
         return rng.permutation(n).astype(np.int32).reshape(T, k)
-    if layout == "expert_sorted":
-        # perm[p] = flattened slot stored at permuted row p (rows grouped by expert).
-        perm = np.argsort(expert_ids.ravel(), kind="stable")
+    if layout == "expert_grouped":
+        # rows ordered by (expert id, random key): grouped by expert, shuffled within
+        row_slot = np.lexsort((rng.random(n), expert_ids.ravel()))
         idx = np.empty(n, dtype=np.int64)
-        idx[perm] = np.arange(n)
+        idx[row_slot] = np.arange(n)
         return idx.astype(np.int32).reshape(T, k)
     raise ValueError(f"unknown layout {layout!r}")
 
 
-def make_finalize_inputs(T: int, H: int, E: int, k: int, seed: int, layout: str = "expert_sorted",
+def make_finalize_inputs(T: int, H: int, E: int, k: int, seed: int, layout: str = "expert_grouped",
                          per_expert: bool = False, residual_std: float = 1.0) -> dict:
     rng = np.random.default_rng(seed)
-    expert_ids, w = topk_softmax_routing(rng, T, E, k)
+    expert_ids, w = draw_routing(rng, T, E, k)
     idx = unpermute_index(rng, expert_ids, layout)
     rows = _normal_bf16(rng, T * k * H).reshape(T * k, H)
     residual = _normal_f32(rng, T * H, residual_std).reshape(T, H)
@@ -158,6 +167,14 @@ def make_per_head_inputs(T: int, heads: int, D: int, seed: int) -> dict:
     return dict(kind="per_head", T=T, heads=heads, D=D, eps=EPS, x=x, gate=gate, gamma=gamma)
 
 
+def make_route_inputs(T: int, E: int, k: int, seed: int, bf16_logits: bool = False) -> dict:
+    rng = np.random.default_rng(seed)
+    logits = _normal_f32(rng, T * E).reshape(T, E)
+    if bf16_logits:
+        logits = bf16_bits_to_f32(to_bf16_bits(logits))
+    return dict(kind="route", T=T, E=E, k=k, logits=logits)
+
+
 def make_inputs(name: str, **overrides) -> dict:
     """Inputs of a named workload; keyword overrides change its sizes or seed."""
     cfg = dict(WORKLOADS[name])
@@ -169,4 +186,6 @@ def make_inputs(name: str, **overrides) -> dict:
         return make_gated_inputs(**cfg)
     if kind == "per_head":
         return make_per_head_inputs(**cfg)
+    if kind == "route":
+        return make_route_inputs(**cfg)
     raise ValueError(kind)
