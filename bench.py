@@ -4,7 +4,7 @@
 
 A step is one pass of the path over one batch of seeded synthetic inputs already resident
 in HBM: for the default workload, one mf_moe_finalize launch at T=16384, H=7168, E=256,
-k=8 (expert-sorted rows), which gathers the k rows, accumulates them in fp32, adds and
+k=8 (rows grouped by expert), which gathers the k rows, accumulates them in fp32, adds and
 stores the residual and emits the RMSNorm output.  W untimed steps, then exactly K timed
 steps between device synchronisations; one JSON line on stdout.
 
@@ -13,7 +13,9 @@ with HIP events around every launch on the stream the kernel runs on; peak 8 TB/
 traffic: HBM bytes per launch measured with rocprofv3 counters, read from the committed
 summary under profiles/ when it was taken from the current kernel sources, else null.
 cpu_baseline: the CPU oracle timed on a bounded sample of the same workload on the host.
-Other workloads (--workload) time the sibling kernels and the copy used for calibration.
+Other workloads (--workload) time the sibling kernels, the routing producer (one step = one
+mf_moe_route call: its three kernels, timed together by the events around the call) and the
+copy used for calibration.
 """
 from __future__ import annotations
 
@@ -36,17 +38,27 @@ CSRC = os.path.join(ROOT, "finalize_residual_rmsnorm_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_digest() -> str:
+# The sources each kind of kernel is built from (launch code included): a counter summary
+# stays valid while these are unchanged.
+KERNEL_SOURCES = {
+    "finalize": ["mf_device.h", "row_norm.h", "finalize_kernel.h", "api_util.h", "mf_api.hip"],
+    "gated": ["mf_device.h", "row_norm.h", "norm_kernels.h", "api_util.h", "mf_api.hip"],
+    "per_head": ["mf_device.h", "norm_kernels.h", "api_util.h", "mf_api.hip"],
+    "copy": ["mf_device.h", "norm_kernels.h", "api_util.h", "mf_api.hip"],
+    "route": ["mf_device.h", "route_kernels.h", "api_util.h", "route_api.hip"],
+}
+
+
+def kernel_source_digest(kind: str = "finalize") -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".h", ".hip")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for name in KERNEL_SOURCES[kind]:
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
-def read_traffic(workload: str):
+def read_traffic(workload: str, kind: str):
     """HBM bytes per launch from the committed counter summary, if it matches the sources."""
     path = os.path.join(PROFILES, f"traffic_{workload}.txt")
     if not os.path.exists(path):
@@ -56,7 +68,7 @@ def read_traffic(workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_digest():
+    if kv.get("kernel_source_sha256") != kernel_source_digest(kind):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -84,6 +96,9 @@ def algorithmic_bytes(d: dict) -> int:
         return n * 6 + d["D"] * 2
     if kind == "copy":
         return 2 * d["bytes"]
+    if kind == "route":
+        T, E, k = d["T"], d["E"], d["k"]
+        return T * E * 4 + T * k * 16 + (E + 1) * 4   # logits in; ids, weights, idx, perm out
     raise ValueError(kind)
 
 
@@ -130,6 +145,14 @@ def upload(d: dict, dev):
         n = d["bytes"] // 4
         return dict(src=torch.randint(0, 1 << 30, (n,), dtype=torch.int32, device=dev),
                     dst=torch.empty(n, dtype=torch.int32, device=dev))
+    if kind == "route":
+        import finalize_residual_rmsnorm_amd as mf
+        T, E, k = d["T"], d["E"], d["k"]
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+        return dict(logits=up(d["logits"]), eids=e((T, k), torch.int32),
+                    w=e((T, k), torch.float32), idx=e((T, k), torch.int32),
+                    perm=e((T * k,), torch.int32), off=e((E + 1,), torch.int32),
+                    ws=e((mf.mf_moe_route_workspace_bytes(T, E, k),), torch.uint8))
     raise ValueError(kind)
 
 
@@ -151,6 +174,10 @@ def launcher(d: dict, g: dict):
                                                   out=g["out"])
     if kind == "copy":
         return lambda: mf.mf_stream_copy(g["src"], g["dst"])
+    if kind == "route":
+        return lambda: mf.mf_moe_route(g["logits"], d["k"], expert_ids=g["eids"], weights=g["w"],
+                                       idx=g["idx"], perm=g["perm"], offsets=g["off"],
+                                       workspace=g["ws"])
     raise ValueError(kind)
 
 
@@ -190,6 +217,8 @@ def cpu_baseline(d: dict, target_cpu_s: float = 15.0, max_threads: int = 16) -> 
                                           d["gamma"], d["eps"])
         elif kind == "per_head":
             oracle.rmsnorm_sigmoid_gate(d["x"][lo:hi], d["gate"][lo:hi], d["gamma"], d["eps"])
+        elif kind == "route":
+            oracle.moe_route(d["logits"][lo:hi], d["k"])
 
     T = d["T"]
     try:
@@ -205,12 +234,20 @@ def cpu_baseline(d: dict, target_cpu_s: float = 15.0, max_threads: int = 16) -> 
     n = max(threads, (n // threads) * threads) if T >= threads else T
     chunk = max(1, n // threads)
     spans = [(i, min(n, i + chunk)) for i in range(0, n, chunk)]
-    t0 = time.perf_counter()
+    # a sample smaller than the target (the whole workload) is run again until about the
+    # target amount of CPU work is done, so the timing is not dominated by thread start-up
     with ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
         list(ex.map(lambda s: run(*s), spans))
-    dt = time.perf_counter() - t0
-    return dict(value=n / dt, unit="tokens/s", cores=min(threads, len(spans)), kind="oracle",
-                sample=f"first {n} of {T} tokens of the same inputs, {len(spans)} threads over "
+        first = time.perf_counter() - t0
+        reps = max(1, int(target_cpu_s / threads / max(first, 1e-9)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            list(ex.map(lambda s: run(*s), spans))
+        dt = time.perf_counter() - t0
+    what = f"the first {n} of {T} tokens" if n < T else f"all {T} tokens"
+    return dict(value=n * reps / dt, unit="tokens/s", cores=min(threads, len(spans)), kind="oracle",
+                sample=f"{what} of the same inputs, {reps} pass(es), {len(spans)} threads over "
                        f"token blocks, {dt:.1f} s wall")
 
 
@@ -224,7 +261,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="finalize_prefill",
                     choices=["finalize_prefill", "finalize_decode_per_expert", "finalize_tiny",
-                             "gated_residual_rmsnorm", "rmsnorm_sigmoid_gate", "stream_copy"])
+                             "gated_residual_rmsnorm", "rmsnorm_sigmoid_gate", "moe_route_prefill",
+                             "moe_route_decode", "stream_copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -272,7 +310,7 @@ def main() -> int:
     ms_per_step = wall * 1e3 / K
 
     achieved = ws / avg_kernel_s / 1e9
-    traffic = read_traffic(args.workload)
+    traffic = read_traffic(args.workload, d["kind"])
     tokens = tokens_of(d)
     value = tokens * K / wall if tokens else ws * K / wall / 1e9
     unit = "tokens/s" if tokens else "GB/s"

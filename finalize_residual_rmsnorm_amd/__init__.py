@@ -1,4 +1,5 @@
-"""Python binding of libmf.so: the MI355X (gfx950) MoE finalize and its two sibling fused norms.
+"""Python binding of libmf.so: the MI355X (gfx950) MoE finalize, its two sibling fused norms and
+the routing producer of the finalize's gather indices.
 
 The functions carry the names of the C entry points in include/mf.h and do argument
 marshalling only: they take torch tensors (device memory), optionally allocate the outputs
@@ -19,7 +20,7 @@ __all__ = [
     "MFError", "lib", "mf_moe_finalize", "mf_gated_residual_rmsnorm", "mf_rmsnorm_sigmoid_gate",
     "mf_moe_finalize_supported", "mf_gated_residual_rmsnorm_supported",
     "mf_rmsnorm_sigmoid_gate_supported", "mf_launch_shape", "mf_stream_copy", "mf_status_string",
-    "LIB_PATH",
+    "mf_moe_route", "mf_moe_route_supported", "mf_moe_route_workspace_bytes", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmf.so")
@@ -56,12 +57,16 @@ def lib() -> ctypes.CDLL:
             "mf_launch_shape": [ci, i64, i32, i32, p, p, p, p],
             "mf_stream_copy": [p, p, i64, p],
             "mf_status_string": [ci],
+            "mf_moe_route": [p, i64, i32, i32, p, p, p, p, p, p, i64, p],
+            "mf_moe_route_supported": [i32, i32],
+            "mf_moe_route_workspace_bytes": [i64, i32, i32],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
         L.mf_status_string.restype = ctypes.c_char_p
+        L.mf_moe_route_workspace_bytes.restype = ctypes.c_int64
         _lib = L
     return _lib
 
@@ -206,3 +211,47 @@ def mf_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
         raise ValueError("mf_stream_copy: size mismatch")
     _check("mf_stream_copy", lib().mf_stream_copy(src.data_ptr(), dst.data_ptr(), n,
                                                   _stream(stream, src.device)))
+
+
+def mf_moe_route_supported(num_experts: int, k: int) -> bool:
+    return bool(lib().mf_moe_route_supported(num_experts, k))
+
+
+def mf_moe_route_workspace_bytes(T: int, num_experts: int, k: int) -> int:
+    """Workspace bytes mf_moe_route needs (raises MFError for unsupported arguments)."""
+    n = lib().mf_moe_route_workspace_bytes(T, num_experts, k)
+    if n < 0:
+        raise MFError("mf_moe_route_workspace_bytes", int(n))
+    return int(n)
+
+
+def mf_moe_route(logits: torch.Tensor, k: int, *, expert_ids: torch.Tensor | None = None,
+                 weights: torch.Tensor | None = None, idx: torch.Tensor | None = None,
+                 perm: torch.Tensor | None = None, offsets: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None, stream=None):
+    """Top-k softmax routing and the expert-sorted permutation of fp32 logits [T, E].
+
+    Returns (expert_ids int32 [T,k], weights fp32 [T,k], idx int32 [T,k], perm int32 [T*k],
+    offsets int32 [E+1]).  Outputs and the workspace (a uint8 tensor of at least
+    mf_moe_route_workspace_bytes(T, E, k) bytes) are allocated with torch when not given.
+    """
+    T, E = logits.shape
+    dev = logits.device
+    ws_bytes = mf_moe_route_workspace_bytes(T, E, k)
+    new = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+    expert_ids = new((T, k), torch.int32) if expert_ids is None else expert_ids
+    weights = new((T, k), torch.float32) if weights is None else weights
+    idx = new((T, k), torch.int32) if idx is None else idx
+    perm = new((T * k,), torch.int32) if perm is None else perm
+    offsets = new((E + 1,), torch.int32) if offsets is None else offsets
+    workspace = new((ws_bytes,), torch.uint8) if workspace is None else workspace
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise TypeError("workspace: expected a 1-d torch.uint8 tensor")
+    st = lib().mf_moe_route(
+        _dev(logits, torch.float32, "logits"), T, E, k,
+        _dev(expert_ids, torch.int32, "expert_ids", (T, k)),
+        _dev(weights, torch.float32, "weights", (T, k)), _dev(idx, torch.int32, "idx", (T, k)),
+        _dev(perm, torch.int32, "perm", (T * k,)), _dev(offsets, torch.int32, "offsets", (E + 1,)),
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream, dev))
+    _check("mf_moe_route", st)
+    return expert_ids, weights, idx, perm, offsets

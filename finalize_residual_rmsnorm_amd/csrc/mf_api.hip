@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "api_util.h"
 #include "finalize_kernel.h"
 #include "mf.h"
 #include "norm_kernels.h"
@@ -24,15 +25,6 @@ constexpr int kMaxVpl = 4;              // plain finalize and gated kernels: 4 x
 constexpr int kMaxVplPerExpert = 8;     // per-expert finalize: 8 x 8 x 512 = 32768
 constexpr int kPerHeadGroupsPerWave = 2;
 
-bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-
-// Do [a, a+na) and [b, b+nb) share a byte?
-bool overlap(const void* a, size_t na, const void* b, size_t nb) {
-    if (!a || !b || na == 0 || nb == 0) return false;
-    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-    return x < y + nb && y < x + na;
-}
-
 bool eps_ok(float eps) { return std::isfinite(eps) && eps >= 0.0f; }
 
 bool row_width_supported(int32_t H) { return H >= 8 && H <= kMaxH && H % 8 == 0; }
@@ -48,12 +40,6 @@ struct RowShape {
     int nr;         // row sums per reduction barrier
     size_t lds;     // dynamic LDS bytes
 };
-
-int pow2_at_least(int n) {
-    int p = 1;
-    while (p < n) p *= 2;
-    return p;
-}
 
 // One slot of 512 values per wave, unless the row needs more than max_waves waves; never more
 // than max_vpl slots per wave (the widest compiled instantiation).
@@ -160,13 +146,6 @@ const void* gated_kernel_for(const RowShape& s) {
         default: return nullptr;
     }
 }
-
-// AMD grids count work-items in 32 bits per dimension.
-bool grid_fits(int64_t blocks, int threads) {
-    return blocks >= 1 && blocks * int64_t(threads) <= int64_t(UINT32_MAX);
-}
-
-int hip_status(hipError_t e) { return e == hipSuccess ? MF_OK : MF_ERR_HIP; }
 
 }  // namespace
 
@@ -359,7 +338,7 @@ const char* mf_status_string(int status) {
         case MF_OK: return "MF_OK: success";
         case MF_ERR_NULL: return "MF_ERR_NULL: a required pointer is NULL";
         case MF_ERR_SHAPE: return "MF_ERR_SHAPE: a size is negative or inconsistent";
-        case MF_ERR_UNSUPPORTED: return "MF_ERR_UNSUPPORTED: width or top-k not supported";
+        case MF_ERR_UNSUPPORTED: return "MF_ERR_UNSUPPORTED: width, expert count or top-k not supported";
         case MF_ERR_ALIGN: return "MF_ERR_ALIGN: a pointer is misaligned";
         case MF_ERR_ALIAS: return "MF_ERR_ALIAS: an output overlaps an input";
         case MF_ERR_VALUE: return "MF_ERR_VALUE: eps must be finite and >= 0";

@@ -1,0 +1,130 @@
+// Host side of the routing entry points declared in include/mf.h: argument checks (before any
+// HIP call), the launch plan and the three launches.  Stateless and allocation-free: the
+// caller passes the workspace.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "api_util.h"
+#include "mf.h"
+#include "route_kernels.h"
+
+namespace {
+
+using namespace mf;
+
+// Routing launch plan.  Kernel 1 runs one wave per `tpw` consecutive tokens, 16 waves per
+// block: tpw grows with T (a power of two, up to 16, and tpw * k <= 256 slots per wave) so that
+// about 4096 waves share the work and the per-block count table stays small.
+struct RoutePlan {
+    int tpw;
+    int64_t nblocks;
+    int id_bits;
+    int epl;  // logits per lane: E <= 64 * epl
+};
+
+bool route_supported(int32_t E, int32_t k) {
+    return E >= 1 && E <= kRouteMaxE && k >= 1 && k <= kRouteMaxK && k <= E;
+}
+
+RoutePlan route_plan(int64_t T, int32_t E, int32_t k) {
+    RoutePlan p;
+    const int64_t want = (T + 4095) / 4096;
+    p.tpw = 1;
+    while (p.tpw < want && p.tpw < 16) p.tpw *= 2;
+    while (p.tpw * k > kRouteSlotsPerWave) p.tpw /= 2;
+    const int64_t tpb = int64_t(kRouteWaves) * p.tpw;
+    p.nblocks = (T + tpb - 1) / tpb;
+    p.id_bits = 0;
+    while ((1 << p.id_bits) < E) ++p.id_bits;
+    p.epl = pow2_at_least((E + kWave - 1) / kWave);
+    return p;
+}
+
+int64_t route_workspace_bytes(const RoutePlan& p, int32_t E) {
+    return (p.nblocks + 1) * int64_t(E) * int64_t(sizeof(int32_t));
+}
+
+const void* route_select_fn(int epl) {
+    switch (epl) {
+        case 1: return reinterpret_cast<const void*>(&route_select_kernel<1>);
+        case 2: return reinterpret_cast<const void*>(&route_select_kernel<2>);
+        case 4: return reinterpret_cast<const void*>(&route_select_kernel<4>);
+        case 8: return reinterpret_cast<const void*>(&route_select_kernel<8>);
+        case 16: return reinterpret_cast<const void*>(&route_select_kernel<16>);
+        default: return nullptr;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int mf_moe_route_supported(int32_t num_experts, int32_t k) { return route_supported(num_experts, k); }
+
+int64_t mf_moe_route_workspace_bytes(int64_t T, int32_t num_experts, int32_t k) {
+    if (T < 0) return MF_ERR_SHAPE;
+    if (!route_supported(num_experts, k)) return MF_ERR_UNSUPPORTED;
+    if (T > INT32_MAX / k) return MF_ERR_SHAPE;  // T * k slots are indexed in int32
+    return route_workspace_bytes(route_plan(T, num_experts, k), num_experts);
+}
+
+int mf_moe_route(const float* logits, int64_t T, int32_t num_experts, int32_t k,
+                 int32_t* expert_ids, float* weights, int32_t* idx, int32_t* perm,
+                 int32_t* expert_offsets, void* workspace, int64_t workspace_bytes,
+                 void* stream) {
+    const int32_t E = num_experts;
+    if (T < 0 || workspace_bytes < 0) return MF_ERR_SHAPE;
+    if (!route_supported(E, k)) return MF_ERR_UNSUPPORTED;
+    if (T > INT32_MAX / k) return MF_ERR_SHAPE;  // T * k slots are indexed in int32
+    const RoutePlan p = route_plan(T, E, k);
+    if (p.nblocks > INT32_MAX || !grid_fits(std::max<int64_t>(p.nblocks, 1), kRouteWaves * kWave))
+        return MF_ERR_SHAPE;
+    if (workspace_bytes < route_workspace_bytes(p, E)) return MF_ERR_SHAPE;
+    if (!expert_offsets || !workspace) return MF_ERR_NULL;
+    if (T > 0 && (!logits || !expert_ids || !weights || !idx || !perm)) return MF_ERR_NULL;
+    const void* ptrs[] = {logits, expert_ids, weights, idx, perm, expert_offsets, workspace};
+    for (const void* q : ptrs)
+        if (!aligned(q, 4)) return MF_ERR_ALIGN;
+    const size_t tk = size_t(T) * k * 4;
+    const size_t ws = size_t(route_workspace_bytes(p, E));
+    const size_t sizes[] = {size_t(T) * E * 4, tk, tk, tk, tk, size_t(E + 1) * 4, ws};
+    for (int i = 0; i < 7; ++i)
+        for (int j = i + 1; j < 7; ++j)
+            if (overlap(ptrs[i], sizes[i], ptrs[j], sizes[j])) return MF_ERR_ALIAS;
+
+    RouteArgs a;
+    a.logits = logits;
+    a.expert_ids = expert_ids;
+    a.weights = weights;
+    a.idx = idx;
+    a.perm = perm;
+    a.offsets = expert_offsets;
+    a.counts = static_cast<int32_t*>(workspace);
+    a.totals = a.counts + p.nblocks * E;
+    a.T = T;
+    a.E = E;
+    a.k = k;
+    a.tpw = p.tpw;
+    a.nblocks = int32_t(p.nblocks);
+    a.id_bits = p.id_bits;
+    void* args[] = {&a};
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (p.nblocks > 0) {
+        const hipError_t e = hipLaunchKernel(route_select_fn(p.epl), dim3(unsigned(p.nblocks)),
+                                             dim3(kRouteWaves * kWave), args,
+                                             route_select_lds_bytes(E), s);
+        if (e != hipSuccess) return MF_ERR_HIP;
+    }
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&route_scan_kernel),
+                                   dim3(unsigned((E + kWave - 1) / kWave)),
+                                   dim3(kRouteWaves * kWave), args, 0, s);
+    if (e != hipSuccess) return MF_ERR_HIP;
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&route_scatter_kernel),
+                        dim3(unsigned(std::max<int64_t>(p.nblocks, 1))),
+                        dim3(kRouteScatterThreads), args, 0, s);
+    return hip_status(e);
+}
+
+}  // extern "C"

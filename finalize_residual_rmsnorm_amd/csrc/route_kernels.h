@@ -1,0 +1,363 @@
+// MoE routing and the expert-sorted permutation on gfx950: the producer of the finalize's
+// gather indices and weights.
+//
+// For T tokens with router logits [T, E] (fp32):
+//   expert_ids[t, j]  the experts of the k largest logits, largest first; among equal logits
+//                     the lower expert id first
+//   weights[t, j]     softmax over those k logits: exp(l_j - l_0) / sum_i exp(l_i - l_0), the
+//                     sum taken in j order (fp32)
+//   offsets[e]        slots routed to experts below e, offsets[E] = T*k: the per-expert row
+//                     ranges of the grouped GEMM (its m_indptr / token_offset argument, page
+//                     "FlashInfer: fused kernels and an optimised scheduler for MoE" (PR #4130),
+//                     code analysis items 1 and 2)
+//   perm[p]           the slot s = t*k + j stored at permuted row p: rows grouped by expert,
+//                     slots ascending within an expert (a stable sort of the slots by expert)
+//   idx[t, j]         the permuted row of slot (t, j), idx[perm[p]] = p: what the finalize
+//                     gathers with
+//
+// Three launches:
+//  1. route_select_kernel: one wave per run of `tpw` consecutive tokens, 16 waves per block.
+//     Top-k in k rounds: the wave-wide maximum of the order-preserving 32-bit image of the
+//     logits (DPP max within rows of 16 lanes, then across the four rows), then a ballot per
+//     logit register finds the lowest expert id holding that maximum (exact and tie-correct),
+//     whose logit is retired; the softmax; then each wave ranks its own slots (contiguous, in
+//     slot order) by expert in 64-slot chunks: a slot's rank among the earlier slots of its chunk with the same
+//     expert comes from ballots over the bits of the expert id (the ballot / prefix-count
+//     technique of the PR #4130 page's warp-cooperative scheduler, "why is this good" item 2),
+//     added to the wave's running per-expert count in LDS.  The waves' counts are scanned in
+//     wave order; idx receives each slot's rank within its block, the workspace the block's
+//     per-expert counts.
+//  2. route_scan_kernel: per expert, the exclusive scan of the block counts over the blocks
+//     (in place) and the expert's total.
+//  3. route_scatter_kernel: one thread per expert: offsets = exclusive scan of the totals over
+//     the experts, and a per-block LDS table offsets[e] + block prefix[e]; then for every slot
+//     p = table[e] + rank: idx[s] = p, perm[p] = s.
+// Everything but the weights is integer work, exact and independent of the launch shape.
+#pragma once
+
+#include "mf_device.h"
+
+namespace mf {
+
+struct RouteArgs {
+    const float* logits;   // [T, E]
+    int32_t* expert_ids;   // [T, k]
+    float* weights;        // [T, k]
+    int32_t* idx;          // [T, k]: rank within the block after kernel 1, the row after kernel 3
+    int32_t* perm;         // [T*k]
+    int32_t* offsets;      // [E + 1]
+    int32_t* counts;       // workspace [nblocks, E]: block counts, then their prefix over blocks
+    int32_t* totals;       // workspace [E]
+    int64_t T;
+    int32_t E;
+    int32_t k;
+    int32_t tpw;           // tokens per wave in kernel 1 (tpw * k <= kRouteSlotsPerWave)
+    int32_t nblocks;       // blocks of kRouteWaves * tpw tokens
+    int32_t id_bits;       // 2^id_bits >= E
+};
+
+constexpr int kRouteMaxK = 16;
+constexpr int kRouteMaxE = 1024;
+constexpr int kRouteWaves = 16;          // waves per block of kernels 1 and 2
+constexpr int kRouteSlotsPerWave = 256;  // 4 chunks of 64 slots
+constexpr int kRouteChunks = kRouteSlotsPerWave / kWave;
+constexpr int kRouteScatterThreads = kRouteMaxE;  // one thread per expert
+constexpr int kRouteScatterSlots = kRouteWaves * kRouteSlotsPerWave / kRouteScatterThreads;
+
+// LDS of kernel 1: per-wave per-expert counts and the wave's expert ids in slot order (both
+// 16-bit: a wave holds at most 256 slots and a block 4096).
+constexpr size_t route_select_lds_bytes(int E) {
+    return size_t(kRouteWaves) * (E + kRouteSlotsPerWave) * sizeof(uint16_t);
+}
+
+// Orders the program-order LDS accesses of one wave's lanes (no hardware wait needed:
+// a wave's LDS instructions complete in order).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Order-preserving map of a float to uint32 (-0 is taken as +0, so it ties with +0).  Every
+// non-NaN value maps to 1 or more (the one NaN pattern that would map to 0 is raised to 1), so
+// 0 can mark "no expert": retired logits and lanes past E.
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+    const uint32_t b = __float_as_uint(v + 0.0f);
+    const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return o > 1u ? o : 1u;
+}
+
+__device__ __forceinline__ float from_ordered_bits(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Maximum over the 64 lanes (every lane active), wave-uniform: within each row of 16 lanes
+// through DPP (quad swaps, half-row mirror, row mirror), then over the four rows.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = umax(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = umax(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = umax(v, dpp_u32<0x141>(v));  // row_half_mirror
+    v = umax(v, dpp_u32<0x140>(v));  // row_mirror
+    const uint32_t a = umax(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16));
+    const uint32_t b = umax(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48));
+    return umax(a, b);
+}
+
+// Logits of one token: lane l holds experts q*64 + l.  The loads are unconditional (lanes past
+// E read expert E-1 and their value is ignored): with no branch around them the compiler can
+// wait for exactly the loads a use needs, so the next token's loads stay in flight.
+template <int EPL>
+__device__ __forceinline__ void load_logits(float (&x)[EPL], const float* row, int E, int lane) {
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) {
+        const int e = q * kWave + lane;
+        x[q] = ld_stream(row + (e < E ? e : E - 1));
+    }
+}
+
+// EPL: logits per lane, E <= 64 * EPL.
+template <int EPL>
+__global__ void __launch_bounds__(kRouteWaves * kWave) route_select_kernel(const RouteArgs a) {
+    extern __shared__ uint16_t route_lds[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int E = a.E, k = a.k;
+    uint16_t* cnt = route_lds;                                     // [kRouteWaves][E]
+    uint16_t* mycnt = cnt + wave * E;
+    uint16_t* stage = route_lds + kRouteWaves * E + wave * kRouteSlotsPerWave;
+
+    const int64_t tw0 = (int64_t(blockIdx.x) * kRouteWaves + wave) * a.tpw;
+    const int ntok = a.T - tw0 <= 0 ? 0 : (a.T - tw0 < a.tpw ? int(a.T - tw0) : a.tpw);
+    for (int e = lane; e < E; e += kWave) mycnt[e] = 0;
+
+    // --- top-k and softmax, one token at a time; the next token's logits are in flight ---
+    float x[EPL], xn[EPL];
+    if (ntok > 0) load_logits(x, a.logits + tw0 * E, E, lane);
+    for (int i = 0; i < ntok; ++i) {
+        const int64_t t = tw0 + i;
+        // the next token's logits (the last token re-reads its own row: no branch, in bounds)
+        load_logits(xn, a.logits + (i + 1 < ntok ? t + 1 : t) * E, E, lane);
+        uint32_t o[EPL];
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) o[q] = q * kWave + lane < E ? ordered_bits(x[q]) : 0u;
+        int my_e = 0;
+        float my_v = 0.0f, top = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kRouteMaxK; ++j) {
+            if (j < k) {
+                uint32_t lm = o[0];
+#pragma unroll
+                for (int q = 1; q < EPL; ++q) lm = umax(lm, o[q]);
+                // m >= 1: k <= E leaves an unretired expert in every round
+                const uint32_t m = wave_max_u32(lm);
+                // the lowest expert id q*64 + lane holding m: the first register q with a match,
+                // then its lowest lane
+                int wq = 0;
+                uint64_t hit = 0;
+#pragma unroll
+                for (int q = EPL - 1; q >= 0; --q) {
+                    const uint64_t bq = __builtin_amdgcn_ballot_w64(o[q] == m);
+                    if (bq) {
+                        wq = q;
+                        hit = bq;
+                    }
+                }
+                const int wl = __builtin_ctzll(hit);
+#pragma unroll
+                for (int q = 0; q < EPL; ++q)
+                    if (q == wq && lane == wl) o[q] = 0u;  // retired
+                const float v = from_ordered_bits(m);
+                if (j == 0) top = v;
+                if (lane == j) {
+                    my_e = wq * kWave + wl;
+                    my_v = v;
+                }
+            }
+        }
+        const float ex = expf(my_v - top);
+        float sum = 0.0f;
+        for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+        if (lane < k) {
+            a.expert_ids[t * k + lane] = my_e;
+            a.weights[t * k + lane] = ex / sum;
+            stage[i * k + lane] = uint16_t(my_e);
+        }
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) x[q] = xn[q];
+    }
+    wave_sync();
+
+    // --- rank of each slot among the wave's earlier slots of the same expert ---
+    const int ns = ntok * k;
+    int rank[kRouteChunks], ce[kRouteChunks];
+#pragma unroll
+    for (int c = 0; c < kRouteChunks; ++c) {
+        rank[c] = 0;
+        ce[c] = 0;
+        if (c * kWave < ns) {
+            const int sl = c * kWave + lane;
+            const bool valid = sl < ns;
+            const int e = valid ? stage[sl] : 0;
+            // m: the chunk's lanes whose expert has every id bit equal to this lane's
+            uint64_t m = __builtin_amdgcn_ballot_w64(valid);
+            for (int b = 0; b < a.id_bits; ++b) {
+                const bool bit = (e >> b) & 1;
+                const uint64_t bb = __builtin_amdgcn_ballot_w64(bit);
+                m &= bit ? bb : ~bb;
+            }
+            const int below = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0));
+            const int base = valid ? mycnt[e] : 0;
+            rank[c] = base + below;
+            ce[c] = e;
+            wave_sync();
+            if (valid && (m >> lane) == 1) mycnt[e] = uint16_t(base + below + 1);  // last of its expert
+            wave_sync();
+        }
+    }
+    __syncthreads();
+    // waves' counts -> exclusive prefix over the waves, in wave order; block totals out
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int c[kRouteWaves];
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) c[w] = cnt[w * E + e];
+        int run = 0;
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) {
+            cnt[w * E + e] = uint16_t(run);
+            run += c[w];
+        }
+        a.counts[int64_t(blockIdx.x) * E + e] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < kRouteChunks; ++c) {
+        const int sl = c * kWave + lane;
+        if (sl < ns) a.idx[tw0 * k + sl] = rank[c] + mycnt[ce[c]];
+    }
+}
+
+// Grid: ceil(E / 64) blocks of kRouteWaves waves; lane = expert, wave = a run of blocks.  Runs
+// of up to kScanRegs blocks stay in registers between the sum and the rewrite.
+constexpr int kScanRegs = 16;
+
+__global__ void __launch_bounds__(kRouteWaves * kWave) route_scan_kernel(const RouteArgs a) {
+    __shared__ int32_t wsum[kRouteWaves][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int E = a.E, nb = a.nblocks;
+    const int e = blockIdx.x * kWave + lane;
+    const bool valid = e < E;
+    const int per = (nb + kRouteWaves - 1) / kRouteWaves;
+    const int b0 = wave * per < nb ? wave * per : nb;
+    const int b1 = b0 + per < nb ? b0 + per : nb;
+    int32_t* col = a.counts + (valid ? e : E - 1);
+    int v[kScanRegs];
+    int sum = 0;
+    if (per <= kScanRegs) {
+        // unconditional loads (clamped into the wave's run) so that all are in flight at once
+        if (b0 < b1) {
+#pragma unroll
+            for (int i = 0; i < kScanRegs; ++i) v[i] = col[int64_t(b0 + i < b1 ? b0 + i : b1 - 1) * E];
+        }
+#pragma unroll
+        for (int i = 0; i < kScanRegs; ++i) {
+            v[i] = valid && b0 + i < b1 ? v[i] : 0;
+            sum += v[i];
+        }
+    } else if (valid) {
+#pragma unroll 8
+        for (int b = b0; b < b1; ++b) sum += col[int64_t(b) * E];
+    }
+    wsum[wave][lane] = sum;
+    __syncthreads();
+    int run = 0;
+    for (int w = 0; w < wave; ++w) run += wsum[w][lane];
+    if (per <= kScanRegs) {
+#pragma unroll
+        for (int i = 0; i < kScanRegs; ++i) {
+            if (valid && b0 + i < b1) col[int64_t(b0 + i) * E] = run;
+            run += v[i];
+        }
+    } else if (valid) {
+        for (int b = b0; b < b1; ++b) {
+            const int c = col[int64_t(b) * E];
+            col[int64_t(b) * E] = run;
+            run += c;
+        }
+    }
+    if (valid && wave == kRouteWaves - 1) a.totals[e] = run;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(v, d);
+        if (lane >= d) v += y;
+    }
+    return v;
+}
+
+// Grid: max(nblocks, 1) blocks of kRouteScatterThreads (one thread per expert).
+__global__ void __launch_bounds__(kRouteScatterThreads) route_scatter_kernel(const RouteArgs a) {
+    __shared__ int32_t tab[kRouteMaxE];
+    __shared__ int32_t wtot[kRouteScatterThreads / kWave];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int E = a.E, k = a.k;
+    const int64_t total = a.T * k;
+    const int64_t per = int64_t(kRouteWaves) * a.tpw * k;
+    const int64_t s0 = int64_t(blockIdx.x) * per;
+    const int64_t s1 = s0 + per < total ? s0 + per : total;
+    // the block's slots: loaded first, they depend on nothing below
+    // (unconditional loads, clamped into range, so that all are in flight at once)
+    int se[kRouteScatterSlots], sr[kRouteScatterSlots];
+    const int e = tid;
+    const int ec = e < E ? e : E - 1;
+    int v = a.totals[ec];
+    int c = 0;
+    if (s0 < s1) {  // false only for the single block of T == 0
+#pragma unroll
+        for (int i = 0; i < kRouteScatterSlots; ++i) {
+            const int64_t s = s0 + tid + int64_t(i) * kRouteScatterThreads;
+            se[i] = a.expert_ids[s < s1 ? s : s1 - 1];
+            sr[i] = a.idx[s < s1 ? s : s1 - 1];
+        }
+        c = a.counts[int64_t(blockIdx.x) * E + ec];
+    }
+    v = e < E ? v : 0;
+    c = e < E ? c : 0;
+    const int incl = wave_inclusive_scan(v, lane);
+    if (lane == kWave - 1) wtot[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wtot[w];
+    const int off = before + incl - v;  // slots routed to experts below e
+    if (e < E) tab[e] = off + c;
+    if (blockIdx.x == 0 && e < E) {
+        a.offsets[e] = off;
+        if (e == E - 1) a.offsets[E] = off + v;  // the total T*k
+    }
+    __syncthreads();
+    if (s0 >= s1) return;
+#pragma unroll
+    for (int i = 0; i < kRouteScatterSlots; ++i) {
+        const int64_t s = s0 + tid + int64_t(i) * kRouteScatterThreads;
+        const int ex = se[i];
+        if (s >= s1 || ex < 0 || ex >= E) continue;  // ids are always below E
+        const int64_t p = int64_t(tab[ex]) + sr[i];
+        if (p < 0 || p >= total) continue;  // never taken: the ranks of an expert are distinct
+        a.idx[s] = int32_t(p);
+        a.perm[p] = int32_t(s);
+    }
+}
+
+}  // namespace mf

@@ -9,6 +9,8 @@
  *           2.4 (MoE finalize + RMSNorm + all-reduce) and the "Fixed-Width Fused Norms" docs.
  *  [PR4730] "MoE all-reduce fusion for Blackwell: FlashInfer's Cake backend", section 2
  *           (fusion strategy: expert sum, residual add and RMSNorm in one launch).
+ *  [PR4130] "FlashInfer: fused kernels and an optimised scheduler for MoE", code analysis
+ *           items 1-3 (grouped GEMM over m_indptr rows; the warp-cooperative scheduler).
  *
  * Conventions for every entry point:
  *  - Tensors are dense and row-major.  bfloat16 data is passed as raw 16-bit patterns
@@ -19,7 +21,7 @@
  *    The library never synchronizes.
  *  - Arguments are checked on the host before any HIP call.  On a failed check the function
  *    returns a negative mf_status and launches nothing.  A zero token count returns MF_OK
- *    without a launch.
+ *    without a launch (mf_moe_route still writes its expert_offsets).
  *  - Row pointers (bf16 and fp32 tensors with H or head_dim columns) must be 16-byte
  *    aligned; idx, weights and expert_ids 4-byte aligned.
  *  - Results are deterministic: the same inputs give bit-identical outputs, whatever the
@@ -71,9 +73,8 @@ typedef enum mf_status {
  *                residual (in-place update of the residual stream); partial overlap is
  *                rejected.
  *  gamma         bf16 [H]; eps >= 0; out bf16 [T, H].
- * Supported: H % 8 == 0 and 8 <= H <= 131072; 1 <= k <= 64 (k <= 16 with the per-expert
- * variant).  Out-of-range idx or expert_ids are clamped into range (memory-safe, result
- * unspecified for that token).
+ * Supported: H % 8 == 0 and 8 <= H <= 32768; 1 <= k <= 64 (both variants).  Out-of-range
+ * idx or expert_ids are clamped into range (memory-safe, result unspecified for that token).
  */
 int mf_moe_finalize(const uint16_t* expert_rows, int64_t num_rows, const int32_t* idx,
                     const float* weights, const int32_t* expert_ids,
@@ -87,7 +88,7 @@ int mf_moe_finalize(const uint16_t* expert_rows, int64_t num_rows, const int32_t
  *   residual_out = residual + sigmoid(gate) * x                 (fp32, sigmoid = 1/(1+e^-g))
  *   out = bf16_rne(residual_out * (mean(residual_out^2) + eps)^-1/2 * gamma)
  *  x, gate bf16 [T, H]; residual, residual_out fp32 [T, H] (may be equal); gamma bf16 [H];
- *  out bf16 [T, H].  Supported: H % 8 == 0 and 8 <= H <= 131072.
+ *  out bf16 [T, H].  Supported: H % 8 == 0 and 8 <= H <= 32768.
  */
 int mf_gated_residual_rmsnorm(const uint16_t* x, const uint16_t* gate, const float* residual,
                               float* residual_out, const uint16_t* gamma, float eps,
@@ -104,12 +105,55 @@ int mf_rmsnorm_sigmoid_gate(const uint16_t* x, const uint16_t* gate, const uint1
                             int32_t head_dim, void* stream);
 
 /*
+ * MoE routing and the expert-sorted permutation: the producer of the finalize's idx and
+ * weights, and of the per-expert row ranges of the grouped GEMM that writes expert_rows
+ * ([PR4130] code analysis items 1-3: the m_indptr / token_offset layout of the grouped GEMM
+ * and its warp-cooperative prefix-count scheduler; the finalize gathers through idx, [PR5319]
+ * section 1).
+ *
+ * For every token t in [0, T), with logits fp32 [T, E]:
+ *   expert_ids[t, 0..k-1] = the experts of the k largest logits of row t, largest first; equal
+ *                           logits go to the lower expert id first (-0 equals +0)
+ *   weights[t, j]         = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0)   (fp32; the softmax over
+ *                           the k selected logits, l_j = logits[t, expert_ids[t, j]])
+ * and over the T*k slots s = t*k + j:
+ *   expert_offsets[e]     = number of slots routed to experts below e; expert_offsets[E] = T*k
+ *   perm[p]               = the slot at permuted row p: slots grouped by expert in expert
+ *                           order, ascending slot order within an expert (a stable sort)
+ *   idx[t, j]             = the permuted row of slot (t, j); idx[perm[p]] = p
+ *
+ *  logits        fp32 [T, E], finite (NaN logits give in-range experts, otherwise unspecified).
+ *  expert_ids    int32 [T, k], weights fp32 [T, k], idx int32 [T, k], perm int32 [T*k],
+ *                expert_offsets int32 [E + 1]: outputs, all written by the call.
+ *  workspace     device memory of at least mf_moe_route_workspace_bytes(T, E, k) bytes,
+ *                4-byte aligned, owned by the caller; its contents on entry do not matter and
+ *                on exit are unspecified.  Calls that share a workspace must not overlap.
+ * Supported: 1 <= E <= 1024 and 1 <= k <= min(E, 16); T * k < 2^31.  Everything but the
+ * weights is exact integer work; the weights are fp32 (expf, a sum in j order, a division).
+ * T == 0 writes expert_offsets (all zero) and nothing else.  No output may overlap another,
+ * the logits or the workspace.
+ */
+int mf_moe_route(const float* logits, int64_t T, int32_t num_experts, int32_t k,
+                 int32_t* expert_ids, float* weights, int32_t* idx, int32_t* perm,
+                 int32_t* expert_offsets, void* workspace, int64_t workspace_bytes,
+                 void* stream);
+
+/*
+ * Workspace bytes mf_moe_route needs: 4 * E * (nblocks + 1), a per-block table of per-expert
+ * counts and the per-expert totals.  nblocks = ceil(T / (16 * tpw)), where tpw (tokens per
+ * wave) is the smallest power of two >= T / 4096, capped at 16 and at 256 / k.  Returns a
+ * negative mf_status for unsupported arguments.
+ */
+int64_t mf_moe_route_workspace_bytes(int64_t T, int32_t num_experts, int32_t k);
+
+/*
  * Capability queries (the fixed-width contract of [PR6544]'s "Fixed-Width Fused Norms":
  * check before calling and fall back otherwise).  Return 1 if supported, else 0.
  */
 int mf_moe_finalize_supported(int32_t H, int32_t k, int per_expert);
 int mf_gated_residual_rmsnorm_supported(int32_t H);
 int mf_rmsnorm_sigmoid_gate_supported(int32_t head_dim);
+int mf_moe_route_supported(int32_t num_experts, int32_t k);
 
 /*
  * Launch shape that mf_moe_finalize / mf_gated_residual_rmsnorm use for a problem size:

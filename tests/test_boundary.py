@@ -25,12 +25,12 @@ G = 0x7F0600000000
 
 def declared_functions():
     text = open(HEADER).read()
-    return re.findall(r"^(?:int|const char\*)\s+(mf_\w+)\(", text, flags=re.M)
+    return re.findall(r"^(?:int|int64_t|const char\*)\s+(mf_\w+)\(", text, flags=re.M)
 
 
 def test_header_symbols_are_exported():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 12, names
     L = ctypes.CDLL(mf.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -54,6 +54,13 @@ def test_supported_queries():
     assert not mf.mf_gated_residual_rmsnorm_supported(8190)
     assert mf.mf_rmsnorm_sigmoid_gate_supported(64)
     assert not mf.mf_rmsnorm_sigmoid_gate_supported(128)
+    assert mf.mf_moe_route_supported(256, 8)
+    assert mf.mf_moe_route_supported(1, 1)
+    assert mf.mf_moe_route_supported(1024, 16)
+    assert not mf.mf_moe_route_supported(1025, 8)
+    assert not mf.mf_moe_route_supported(0, 1)
+    assert not mf.mf_moe_route_supported(256, 17)
+    assert not mf.mf_moe_route_supported(4, 5)             # k > E
 
 
 def fin(rows=A, num_rows=32, idx=B, w=C, eids=None, eg=None, E=0, res=D, res_out=E_,
@@ -174,3 +181,36 @@ def test_binding_refuses_cpu_tensors():
         mf.mf_moe_finalize(x, torch.zeros((2, 2), dtype=torch.int32),
                            torch.zeros((2, 2)), torch.zeros((2, 16)),
                            torch.zeros(16, dtype=torch.bfloat16))
+
+
+def route(logits=A, T=16, E=64, k=4, ids=B, w=C, idx=D, perm=E_, off=F, ws=G, ws_bytes=1 << 20):
+    return mf.lib().mf_moe_route(logits, T, E, k, ids, w, idx, perm, off, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), SHAPE), (dict(ws_bytes=-1), SHAPE), (dict(E=0), UNSUP), (dict(E=1025), UNSUP),
+    (dict(k=0), UNSUP), (dict(k=17), UNSUP), (dict(E=4, k=5), UNSUP),
+    (dict(T=1 << 28, k=8), SHAPE),             # T * k slots must fit int32
+    (dict(ws_bytes=16), SHAPE),                # workspace smaller than required
+    (dict(off=None), NULL), (dict(ws=None), NULL), (dict(logits=None), NULL),
+    (dict(ids=None), NULL), (dict(w=None), NULL), (dict(idx=None), NULL), (dict(perm=None), NULL),
+    (dict(idx=D + 2), ALIGN), (dict(ws=G + 1), ALIGN), (dict(logits=A + 2), ALIGN),
+    (dict(idx=B + 8), ALIAS), (dict(perm=G + 64), ALIAS), (dict(off=A + 4), ALIAS),
+    (dict(ws=C), ALIAS),
+])
+def test_route_rejects_bad_arguments(kw, code):
+    assert route(**kw) == code
+
+
+def test_route_workspace_bytes():
+    f = mf.mf_moe_route_workspace_bytes
+    # 4 * E * (nblocks + 1); a block is 16 waves of tpw tokens
+    assert f(0, 8, 2) == 4 * 8 * 1
+    assert f(1, 8, 2) == 4 * 8 * 2
+    assert f(16384, 256, 8) == 4 * 256 * (16384 // (16 * 4) + 1)     # tpw 4
+    assert f(10 ** 6, 1024, 16) == 4 * 1024 * (-(-10 ** 6 // 256) + 1)  # tpw 16
+    assert f(10 ** 6, 64, 32 // 2) == 4 * 64 * (-(-10 ** 6 // 256) + 1)
+    assert mf.lib().mf_moe_route_workspace_bytes(-1, 8, 2) == SHAPE
+    assert mf.lib().mf_moe_route_workspace_bytes(8, 0, 1) == UNSUP
+    with pytest.raises(mf.MFError):
+        f(8, 4, 5)
