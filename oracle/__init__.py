@@ -1,4 +1,5 @@
-"""CPU oracle for the MoE finalize path, the two sibling fused norms, and the routing and
+"""CPU oracle for the MoE finalize path, the sibling fused norms (gated residual RMSNorm, its
+dual-output "next" form, per-head RMSNorm with a sigmoid gate), and the routing and
 expert-sorted permutation the finalize consumes.
 
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg
@@ -44,6 +45,7 @@ def _load():
         p, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
         lib.oracle_moe_finalize.argtypes = [p, i64, p, p, p, p, i32, p, p, p, f32, p, i64, i32, i32]
         lib.oracle_gated_residual_rmsnorm.argtypes = [p, p, p, p, p, f32, p, i64, i32]
+        lib.oracle_gated_residual_next_rmsnorm.argtypes = [p, p, p, p, p, p, f32, p, p, i64, i32]
         lib.oracle_rmsnorm_sigmoid_gate.argtypes = [p, p, p, f32, p, i64, i32, i32]
         lib.oracle_moe_route.argtypes = [p, i64, i32, i32, p, p, p, p, p]
         lib.oracle_bf16_round.argtypes = [p, p, i64]
@@ -104,6 +106,28 @@ def gated_residual_rmsnorm(x, gate, residual, gamma, eps):
     lib.oracle_gated_residual_rmsnorm(px, pgt, pres, r_out.ctypes.data_as(ctypes.c_void_p), pg,
                                       float(eps), out.ctypes.data_as(ctypes.c_void_p), T, H)
     return r_out, out
+
+
+def gated_residual_next_rmsnorm(x, gate, residual, gamma, gamma_next, eps):
+    """Return (residual_out float32 [T,H], out bf16-bits [T,H], out_next bf16-bits [T,H]).
+
+    The gated residual feeding two RMSNorm outputs (gamma and gamma_next) that share one mean
+    square: the reading taken of the pages' "gated residual dual norm", which they name only.
+    """
+    lib = _load()
+    x, px = _c(x, np.uint16)
+    gt, pgt = _c(gate, np.uint16)
+    res, pres = _c(residual, np.float32)
+    g, pg = _c(gamma, np.uint16)
+    gn, pgn = _c(gamma_next, np.uint16)
+    T, H = x.shape
+    r_out = np.empty((T, H), dtype=np.float32)
+    out = np.empty((T, H), dtype=np.uint16)
+    out_next = np.empty((T, H), dtype=np.uint16)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    lib.oracle_gated_residual_next_rmsnorm(px, pgt, pres, ptr(r_out), pg, pgn, float(eps), ptr(out),
+                                           ptr(out_next), T, H)
+    return r_out, out, out_next
 
 
 def rmsnorm_sigmoid_gate(x, gate, gamma, eps):

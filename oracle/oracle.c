@@ -1,5 +1,11 @@
 /*
- * Plain CPU oracle for the MoE finalize path and its two sibling fused norms.
+ * Plain CPU oracle for the MoE finalize path, its sibling fused norms (gated residual
+ * RMSNorm, the dual-output gated residual norm, per-head RMSNorm with a sigmoid gate), and the
+ * routing that produces the finalize's gather indices and weights.
+ *
+ * Parity unpinned, as to meaning only: the dual-output gated residual norm is named by the
+ * pages but not defined; the reading taken is stated at its function, whose arithmetic the
+ * tests pin.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline leg of
  * the benchmark may load this library.  It shares no code, header, table or helper with
@@ -161,6 +167,40 @@ int oracle_gated_residual_rmsnorm(const uint16_t* x, const uint16_t* gate, const
         double s = rms_scale_f32(r, H, eps);
         uint16_t* o = out + t * (int64_t)H;
         for (int32_t h = 0; h < H; ++h) o[h] = bf16_round((double)r[h] * s * bf16_value(gamma[h]));
+    }
+    return 0;
+}
+
+/*
+ * Gated-residual dual RMSNorm, "gated_residual_next_rmsnorm": the PR #6544 page names it in its
+ * Fixed-Width Fused Norms docs and calls it a "gated residual dual norm" in section 2.2, but
+ * never defines it.  Reading taken: the gated residual of section 1.1 feeds two RMSNorm outputs
+ * that share one mean square, this layer's (gamma) and the next layer's pre-norm (gamma_next):
+ *     r        = fp32(residual + sigmoid(gate) * x)                  (one rounding, as above)
+ *     out      = bf16(r * rms_scale(r) * gamma)
+ *     out_next = bf16(r * rms_scale(r) * gamma_next)
+ * The arithmetic under this reading is pinned by the tests; the reading itself is not fixed by
+ * the pages (parity unpinned as to what the pages mean).
+ */
+int oracle_gated_residual_next_rmsnorm(const uint16_t* x, const uint16_t* gate,
+                                       const float* residual, float* residual_out,
+                                       const uint16_t* gamma, const uint16_t* gamma_next,
+                                       float eps, uint16_t* out, uint16_t* out_next, int64_t T,
+                                       int32_t H) {
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t* xt = x + t * (int64_t)H;
+        const uint16_t* gt = gate + t * (int64_t)H;
+        const float* res = residual + t * (int64_t)H;
+        float* r = residual_out + t * (int64_t)H;
+        for (int32_t h = 0; h < H; ++h)
+            r[h] = (float)((double)res[h] + sigmoid(bf16_value(gt[h])) * bf16_value(xt[h]));
+        double s = rms_scale_f32(r, H, eps);
+        uint16_t* o = out + t * (int64_t)H;
+        uint16_t* on = out_next + t * (int64_t)H;
+        for (int32_t h = 0; h < H; ++h) {
+            o[h] = bf16_round((double)r[h] * s * bf16_value(gamma[h]));
+            on[h] = bf16_round((double)r[h] * s * bf16_value(gamma_next[h]));
+        }
     }
     return 0;
 }

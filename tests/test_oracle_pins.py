@@ -55,6 +55,16 @@ def test_golden_gated_hand_example():
     assert np.array_equal(o, _bits(g["expected_out_bits"]))
 
 
+def test_golden_gated_next_hand_example():
+    g = json.load(open(GOLDEN))["gated_residual_next_rmsnorm"]
+    r, o, on = oracle.gated_residual_next_rmsnorm(
+        _rows_bf16(g["x"]), _rows_bf16(g["gate"]), np.array(g["residual"], np.float32),
+        _rows_bf16(g["gamma"]), _rows_bf16(g["gamma_next"]), g["eps"])
+    assert np.array_equal(r, np.array(g["expected_residual_out"], np.float32))
+    assert np.array_equal(o, _bits(g["expected_out_bits"]))
+    assert np.array_equal(on, _bits(g["expected_out_next_bits"]))
+
+
 def test_golden_per_head_hand_example():
     g = json.load(open(GOLDEN))["rmsnorm_sigmoid_gate"]
     x = _rows_bf16(np.array(g["x"], np.float32).reshape(-1, g["D"])).reshape(np.shape(g["x"]))
@@ -327,6 +337,50 @@ def test_gated_very_negative_gate_keeps_residual():
     gm30 = workloads.to_bf16_bits(np.full(d["gate"].shape, -30.0, np.float32))
     r, _ = oracle.gated_residual_rmsnorm(d["x"], gm30, res, d["gamma"], d["eps"])
     assert np.array_equal(r, res)
+
+
+# ----------------------------------------------------------------------------- gated, dual output
+
+
+def test_gated_next_brute_force():
+    d = workloads.make_gated_inputs(6, 520, seed=27, dual=True)
+    r, o, on = oracle.gated_residual_next_rmsnorm(d["x"], d["gate"], d["residual"], d["gamma"],
+                                                  d["gamma_next"], d["eps"])
+    exact = d["residual"].astype(np.float64) + expit(f32(d["gate"]).astype(np.float64)) * \
+        f32(d["x"]).astype(np.float64)
+    assert np.all(np.abs(r - exact) <= 0.5001 * U32 * 2 * np.abs(exact) + 1e-30)
+    assert _close_bf16(o, _rmsnorm_bits(r, d["gamma"], d["eps"]))
+    assert _close_bf16(on, _rmsnorm_bits(r, d["gamma_next"], d["eps"]))
+
+
+def test_gated_next_equal_gammas_give_equal_outputs():
+    d = workloads.make_gated_inputs(4, 256, seed=28, dual=True)
+    r, o, on = oracle.gated_residual_next_rmsnorm(d["x"], d["gate"], d["residual"], d["gamma"],
+                                                  d["gamma"], d["eps"])
+    assert np.array_equal(o, on)
+
+
+def test_gated_next_double_gamma_doubles_exactly():
+    # gamma_next = 2 * gamma (exact in bf16): every out_next value is exactly twice out's
+    d = workloads.make_gated_inputs(4, 256, seed=29, dual=True)
+    g2 = workloads.to_bf16_bits(2.0 * f32(d["gamma"]))
+    r, o, on = oracle.gated_residual_next_rmsnorm(d["x"], d["gate"], d["residual"], d["gamma"], g2,
+                                                  d["eps"])
+    assert np.array_equal(f32(on), np.float32(2) * f32(o))
+
+
+def test_gated_next_gate_zero_and_unit_gamma_next():
+    # gate = 0: residual_out = residual + x/2 exactly; gamma_next = 1: the RMS of out_next is
+    # sqrt(ms / (ms + eps)) up to bf16 rounding (2^-9 relative per element)
+    d = workloads.make_gated_inputs(5, 1024, seed=30, dual=True)
+    zero = np.zeros_like(d["gate"])
+    one = workloads.to_bf16_bits(np.ones(1024, np.float32))
+    r, o, on = oracle.gated_residual_next_rmsnorm(d["x"], zero, d["residual"], d["gamma"], one,
+                                                  d["eps"])
+    assert np.array_equal(r, d["residual"] + np.float32(0.5) * f32(d["x"]))
+    ms = (r.astype(np.float64) ** 2).mean(axis=1)
+    rms = np.sqrt((f32(on).astype(np.float64) ** 2).mean(axis=1))
+    assert np.allclose(rms, np.sqrt(ms / (ms + d["eps"])), rtol=2.0 ** -8)
 
 
 # ----------------------------------------------------------------------------- per-head

@@ -30,7 +30,8 @@ Recipe (numpy ``default_rng(seed)``, PCG64; draws happen in the order listed):
   makes exactly equal logits common).
 * Gated-residual RMSNorm (``make_gated_inputs``): x ``[T, H]`` ~ N(0, 1) bf16,
   gate ``[T, H]`` ~ N(0, 2) bf16 (standard deviation 2), residual ``[T, H]`` ~ N(0, 1) fp32,
-  gamma ``[H]`` = 1 + 0.1 * N(0, 1) bf16.
+  gamma ``[H]`` = 1 + 0.1 * N(0, 1) bf16; with ``dual=True`` then gamma_next ``[H]``, drawn
+  the same way.
 * Per-head RMSNorm + sigmoid gate (``make_per_head_inputs``): x ``[T, heads, D]`` ~ N(0, 1)
   bf16, gate ``[T, heads, D]`` ~ N(0, 2) bf16, gamma ``[D]`` = 1 + 0.1 * N(0, 1) bf16.
 
@@ -59,6 +60,9 @@ WORKLOADS = {
                              layout="expert_grouped", per_expert=False, residual_std=1.0),
     # Gated-residual RMSNorm at its fixed hidden size.
     "gated_residual_rmsnorm": dict(kind="gated", T=4096, H=8192, seed=4),
+    # The dual-output form: the same gated residual feeding this layer's and the next layer's
+    # RMSNorm (two gammas), at the same fixed hidden size.
+    "gated_residual_next_rmsnorm": dict(kind="gated", T=4096, H=8192, seed=8, dual=True),
     # Per-head RMSNorm + sigmoid gate at its fixed head dim.
     "rmsnorm_sigmoid_gate": dict(kind="per_head", T=4096, heads=64, D=64, seed=5),
     # Routing that produces the prefill finalize's gather indices and weights.
@@ -150,13 +154,17 @@ def make_finalize_inputs(T: int, H: int, E: int, k: int, seed: int, layout: str 
     return d
 
 
-def make_gated_inputs(T: int, H: int, seed: int) -> dict:
+def make_gated_inputs(T: int, H: int, seed: int, dual: bool = False) -> dict:
     rng = np.random.default_rng(seed)
     x = _normal_bf16(rng, T * H).reshape(T, H)
     gate = _normal_bf16(rng, T * H, 2.0).reshape(T, H)
     residual = _normal_f32(rng, T * H).reshape(T, H)
     gamma = to_bf16_bits(1.0 + 0.1 * _normal_f32(rng, H))
-    return dict(kind="gated", T=T, H=H, eps=EPS, x=x, gate=gate, residual=residual, gamma=gamma)
+    d = dict(kind="gated", T=T, H=H, eps=EPS, x=x, gate=gate, residual=residual, gamma=gamma)
+    if dual:
+        d["kind"] = "gated_next"
+        d["gamma_next"] = to_bf16_bits(1.0 + 0.1 * _normal_f32(rng, H))
+    return d
 
 
 def make_per_head_inputs(T: int, heads: int, D: int, seed: int) -> dict:
