@@ -13,7 +13,8 @@ with HIP events around every launch on the stream the kernel runs on; peak 8 TB/
 traffic: HBM bytes per launch measured with rocprofv3 counters, read from the committed
 summary under profiles/ when it was taken from the current kernel sources, else null.
 cpu_baseline: the CPU oracle timed on a bounded sample of the same workload on the host.
-Other workloads (--workload) time the sibling kernels, the routing producer (one step = one
+Other workloads (--workload) time the sibling kernels (the gated norms, single and dual output,
+and the per-head norm), the routing producer (one step = one
 mf_moe_route call: its three kernels, timed together by the events around the call) and the
 copy used for calibration.
 """
@@ -40,11 +41,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 # The sources each kind of kernel is built from (launch code included): a counter summary
 # stays valid while these are unchanged.
+_NORM_SOURCES = ["mf_device.h", "row_norm.h", "norm_kernels.h", "api_util.h", "row_shape.h",
+                 "norm_api.hip"]
 KERNEL_SOURCES = {
-    "finalize": ["mf_device.h", "row_norm.h", "finalize_kernel.h", "api_util.h", "mf_api.hip"],
-    "gated": ["mf_device.h", "row_norm.h", "norm_kernels.h", "api_util.h", "mf_api.hip"],
-    "per_head": ["mf_device.h", "norm_kernels.h", "api_util.h", "mf_api.hip"],
-    "copy": ["mf_device.h", "norm_kernels.h", "api_util.h", "mf_api.hip"],
+    "finalize": ["mf_device.h", "row_norm.h", "finalize_kernel.h", "api_util.h", "row_shape.h",
+                 "mf_api.hip"],
+    "gated": _NORM_SOURCES,
+    "gated_next": _NORM_SOURCES,
+    "per_head": _NORM_SOURCES,
+    "copy": _NORM_SOURCES,
     "route": ["mf_device.h", "route_kernels.h", "api_util.h", "route_api.hip"],
 }
 
@@ -91,6 +96,9 @@ def algorithmic_bytes(d: dict) -> int:
     if kind == "gated":
         T, H = d["T"], d["H"]
         return T * H * (2 + 2 + 4 + 4 + 2) + H * 2
+    if kind == "gated_next":
+        T, H = d["T"], d["H"]
+        return T * H * (2 + 2 + 4 + 4 + 2 + 2) + 2 * H * 2
     if kind == "per_head":
         n = d["T"] * d["heads"] * d["D"]
         return n * 6 + d["D"] * 2
@@ -137,6 +145,12 @@ def upload(d: dict, dev):
                     gamma=up(d["gamma"], True),
                     res_out=torch.empty((T, H), dtype=torch.float32, device=dev),
                     out=torch.empty((T, H), dtype=torch.bfloat16, device=dev))
+    if kind == "gated_next":
+        T, H = d["T"], d["H"]
+        e = lambda dt: torch.empty((T, H), dtype=dt, device=dev)
+        return dict(x=up(d["x"], True), gate=up(d["gate"], True), res=up(d["residual"]),
+                    gamma=up(d["gamma"], True), gamma_next=up(d["gamma_next"], True),
+                    res_out=e(torch.float32), out=e(torch.bfloat16), out_next=e(torch.bfloat16))
     if kind == "per_head":
         x = up(d["x"], True)
         return dict(x=x, gate=up(d["gate"], True), gamma=up(d["gamma"], True),
@@ -169,6 +183,10 @@ def launcher(d: dict, g: dict):
         return lambda: mf.mf_gated_residual_rmsnorm(g["x"], g["gate"], g["res"], g["gamma"],
                                                     d["eps"], residual_out=g["res_out"],
                                                     out=g["out"])
+    if kind == "gated_next":
+        return lambda: mf.mf_gated_residual_next_rmsnorm(
+            g["x"], g["gate"], g["res"], g["gamma"], g["gamma_next"], d["eps"],
+            residual_out=g["res_out"], out=g["out"], out_next=g["out_next"])
     if kind == "per_head":
         return lambda: mf.mf_rmsnorm_sigmoid_gate(g["x"], g["gate"], g["gamma"], d["eps"],
                                                   out=g["out"])
@@ -188,7 +206,7 @@ def launch_config(name: str, d: dict) -> dict:
         pe = d.get("expert_gamma") is not None
         return mf.mf_launch_shape(mf.KIND_FINALIZE_PER_EXPERT if pe else mf.KIND_FINALIZE,
                                   d["T"], d["H"], d["k"])
-    if kind == "gated":
+    if kind in ("gated", "gated_next"):
         return mf.mf_launch_shape(mf.KIND_GATED, d["T"], d["H"])
     return {}
 
@@ -215,6 +233,10 @@ def cpu_baseline(d: dict, target_cpu_s: float = 15.0, max_threads: int = 16) -> 
         elif kind == "gated":
             oracle.gated_residual_rmsnorm(d["x"][lo:hi], d["gate"][lo:hi], d["residual"][lo:hi],
                                           d["gamma"], d["eps"])
+        elif kind == "gated_next":
+            oracle.gated_residual_next_rmsnorm(d["x"][lo:hi], d["gate"][lo:hi],
+                                               d["residual"][lo:hi], d["gamma"], d["gamma_next"],
+                                               d["eps"])
         elif kind == "per_head":
             oracle.rmsnorm_sigmoid_gate(d["x"][lo:hi], d["gate"][lo:hi], d["gamma"], d["eps"])
         elif kind == "route":
@@ -261,7 +283,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="finalize_prefill",
                     choices=["finalize_prefill", "finalize_decode_per_expert", "finalize_tiny",
-                             "gated_residual_rmsnorm", "rmsnorm_sigmoid_gate", "moe_route_prefill",
+                             "gated_residual_rmsnorm", "gated_residual_next_rmsnorm",
+                             "rmsnorm_sigmoid_gate", "moe_route_prefill",
                              "moe_route_decode", "stream_copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

@@ -1,5 +1,5 @@
-"""Python binding of libmf.so: the MI355X (gfx950) MoE finalize, its two sibling fused norms and
-the routing producer of the finalize's gather indices.
+"""Python binding of libmf.so: the MI355X (gfx950) MoE finalize, its sibling fused norms and the
+routing producer of the finalize's gather indices.
 
 The functions carry the names of the C entry points in include/mf.h and do argument
 marshalling only: they take torch tensors (device memory), optionally allocate the outputs
@@ -20,7 +20,8 @@ __all__ = [
     "MFError", "lib", "mf_moe_finalize", "mf_gated_residual_rmsnorm", "mf_rmsnorm_sigmoid_gate",
     "mf_moe_finalize_supported", "mf_gated_residual_rmsnorm_supported",
     "mf_rmsnorm_sigmoid_gate_supported", "mf_launch_shape", "mf_stream_copy", "mf_status_string",
-    "mf_moe_route", "mf_moe_route_supported", "mf_moe_route_workspace_bytes", "LIB_PATH",
+    "mf_moe_route", "mf_moe_route_supported", "mf_moe_route_workspace_bytes",
+    "mf_gated_residual_next_rmsnorm", "mf_gated_residual_next_rmsnorm_supported", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmf.so")
@@ -58,6 +59,8 @@ def lib() -> ctypes.CDLL:
             "mf_stream_copy": [p, p, i64, p],
             "mf_status_string": [ci],
             "mf_moe_route": [p, i64, i32, i32, p, p, p, p, p, p, i64, p],
+            "mf_gated_residual_next_rmsnorm": [p, p, p, p, p, p, f32, p, p, i64, i32, p],
+            "mf_gated_residual_next_rmsnorm_supported": [i32],
             "mf_moe_route_supported": [i32, i32],
             "mf_moe_route_workspace_bytes": [i64, i32, i32],
         }
@@ -159,6 +162,33 @@ def mf_gated_residual_rmsnorm(x: torch.Tensor, gate: torch.Tensor, residual: tor
     return out, residual_out
 
 
+def mf_gated_residual_next_rmsnorm(x: torch.Tensor, gate: torch.Tensor, residual: torch.Tensor,
+                                   gamma: torch.Tensor, gamma_next: torch.Tensor,
+                                   eps: float = 1e-6, *,
+                                   residual_out: torch.Tensor | None = None,
+                                   out: torch.Tensor | None = None,
+                                   out_next: torch.Tensor | None = None, stream=None):
+    """Gated-residual dual RMSNorm.  Returns (out, out_next bf16 [T,H], residual_out fp32 [T,H])."""
+    T, H = x.shape
+    dev = x.device
+    if residual_out is None:
+        residual_out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if out_next is None:
+        out_next = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    st = lib().mf_gated_residual_next_rmsnorm(
+        _dev(x, torch.bfloat16, "x"), _dev(gate, torch.bfloat16, "gate", (T, H)),
+        _dev(residual, torch.float32, "residual", (T, H)),
+        _dev(residual_out, torch.float32, "residual_out", (T, H)),
+        _dev(gamma, torch.bfloat16, "gamma", (H,)),
+        _dev(gamma_next, torch.bfloat16, "gamma_next", (H,)), float(eps),
+        _dev(out, torch.bfloat16, "out", (T, H)), _dev(out_next, torch.bfloat16, "out_next", (T, H)),
+        T, H, _stream(stream, dev))
+    _check("mf_gated_residual_next_rmsnorm", st)
+    return out, out_next, residual_out
+
+
 def mf_rmsnorm_sigmoid_gate(x: torch.Tensor, gate: torch.Tensor, gamma: torch.Tensor,
                             eps: float = 1e-6, *, out: torch.Tensor | None = None, stream=None):
     """Per-head RMSNorm + sigmoid gate over x [T, heads, head_dim].  Returns out (bf16)."""
@@ -180,6 +210,10 @@ def mf_moe_finalize_supported(H: int, k: int, per_expert: bool = False) -> bool:
 
 def mf_gated_residual_rmsnorm_supported(H: int) -> bool:
     return bool(lib().mf_gated_residual_rmsnorm_supported(H))
+
+
+def mf_gated_residual_next_rmsnorm_supported(H: int) -> bool:
+    return bool(lib().mf_gated_residual_next_rmsnorm_supported(H))
 
 
 def mf_rmsnorm_sigmoid_gate_supported(head_dim: int) -> bool:

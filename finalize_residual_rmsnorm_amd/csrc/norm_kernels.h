@@ -14,23 +14,62 @@ namespace mf {
 // Same row mapping and fixed reduction tree as the finalize kernel.  The sigmoid uses the
 // hardware exp2 and an IEEE division so that residual_out stays within a few fp32 ulps of
 // the exact value; that keeps the kernel bound by HBM rather than by the transcendental.
+//
+// DUAL: the dual-output form (gated_residual_next_rmsnorm, named by the same page's docs and
+// its section 2.2 "gated residual dual norm", not defined there).  Reading taken: the one
+// gated residual and its one mean square feed two outputs, this layer's RMSNorm (gamma) and
+// the next layer's (gamma_next):
+//   out_next = bf16(residual_out * (mean(residual_out^2) + eps)^-1/2 * gamma_next)
+// out is computed exactly as without DUAL, so it is bit-identical to the single-output form.
 struct GatedArgs {
-    const uint16_t* x;       // bf16 [T, H]
-    const uint16_t* gate;    // bf16 [T, H]
-    const float* residual;   // [T, H]
-    float* residual_out;     // [T, H], may equal residual
-    const uint16_t* gamma;   // bf16 [H]
-    uint16_t* out;           // bf16 [T, H]
+    const uint16_t* x;           // bf16 [T, H]
+    const uint16_t* gate;        // bf16 [T, H]
+    const float* residual;       // [T, H]
+    float* residual_out;         // [T, H], may equal residual
+    const uint16_t* gamma;       // bf16 [H]
+    uint16_t* out;               // bf16 [T, H]
+    const uint16_t* gamma_next;  // bf16 [H] (DUAL only)
+    uint16_t* out_next;          // bf16 [T, H] (DUAL only)
     int64_t T;
     int32_t H;
     float eps;
 };
 
+// The final RMSNorm of a row into two bf16 outputs with one mean square: the same arithmetic
+// as rmsnorm_store, applied with each gamma.
+template <int VPL, int TAIL>
+__device__ __forceinline__ void rmsnorm_store_dual(const float (&r)[VPL][8], const u32x4 (&g)[VPL],
+                                                   const u32x4 (&gn)[VPL],
+                                                   const Slots<VPL, TAIL>& sl, uint16_t* out_row,
+                                                   uint16_t* next_row, int H, float eps,
+                                                   TokenLds& L, const RowMap& m) {
+    float ss[1] = {lane_sumsq(r, sl)};
+    token_sum<1>(ss, L, m);
+    const float inv = 1.0f / __builtin_sqrtf(ss[0] / (float)H + eps);
+#pragma unroll
+    for (int s = 0; s < VPL; ++s) {
+        float gf[8], gnf[8];
+        widen8(g[s], gf);
+        widen8(gn[s], gnf);
+        u32x4 o, on;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float y0 = r[s][2 * i] * inv, y1 = r[s][2 * i + 1] * inv;
+            o[i] = pack_bf16x2(y0 * gf[2 * i], y1 * gf[2 * i + 1]);
+            on[i] = pack_bf16x2(y0 * gnf[2 * i], y1 * gnf[2 * i + 1]);
+        }
+        if (sl.sval[s]) {
+            *at<u32x4>(out_row, sl.eoff[s] * 2u) = o;
+            *at<u32x4>(next_row, sl.eoff[s] * 2u) = on;
+        }
+    }
+}
+
 __device__ __forceinline__ float sigmoid_accurate(float g) {
     return 1.0f / (1.0f + __expf(-g));
 }
 
-template <int VPL, int TAIL>
+template <int VPL, int TAIL, bool DUAL>
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(VPL == 1 ? 7 : 4, 8)))
 gated_residual_rmsnorm_kernel(const GatedArgs a) {
     extern __shared__ float lds[];
@@ -42,7 +81,7 @@ gated_residual_rmsnorm_kernel(const GatedArgs a) {
     const uint16_t* gr = a.gate + row;
     const float* res = a.residual + row;
 
-    u32x4 xv[VPL], gv[VPL], gm[VPL];
+    u32x4 xv[VPL], gv[VPL], gm[VPL], gn[VPL];
     f32x4 rv[VPL][2];
 #pragma unroll
     for (int s = 0; s < VPL; ++s) {
@@ -52,6 +91,7 @@ gated_residual_rmsnorm_kernel(const GatedArgs a) {
         rv[s][1] = ld_stream(at<f32x4>(res, sl.eoff[s] * 4u + 16u));
     }
     load_gamma(gm, a.gamma, sl);
+    if constexpr (DUAL) load_gamma(gn, a.gamma_next, sl);
     float r[VPL][8];
 #pragma unroll
     for (int s = 0; s < VPL; ++s) {
@@ -66,7 +106,10 @@ gated_residual_rmsnorm_kernel(const GatedArgs a) {
     }
     store_residual(r, sl, a.residual_out + row);
     TokenLds L = token_lds(lds, m.wpt, 1);
-    rmsnorm_store(r, gm, sl, a.out + row, H, a.eps, L, m);
+    if constexpr (DUAL)
+        rmsnorm_store_dual(r, gm, gn, sl, a.out + row, a.out_next + row, H, a.eps, L, m);
+    else
+        rmsnorm_store(r, gm, sl, a.out + row, H, a.eps, L, m);
 }
 
 // ---------------------------------------------------------------------------------------

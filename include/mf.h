@@ -1,5 +1,6 @@
 /*
- * mf.h - C ABI of the MI355X (gfx950) MoE finalize library and its two sibling fused norms.
+ * mf.h - C ABI of the MI355X (gfx950) MoE finalize library, its sibling fused norms and the
+ * routing producer of its inputs.
  *
  * Sources of the operations (pages on FlashInfer pull requests; section names as on each page):
  *  [PR5319] "FlashInfer MoE performance: improving the deterministic finalize with CuTe DSL",
@@ -95,6 +96,24 @@ int mf_gated_residual_rmsnorm(const uint16_t* x, const uint16_t* gate, const flo
                               uint16_t* out, int64_t T, int32_t H, void* stream);
 
 /*
+ * Gated-residual dual RMSNorm ("gated_residual_next_rmsnorm": named by [PR6544]'s fixed-width
+ * norm docs and its section 2.2 "gated residual dual norm", not defined there).  Reading taken:
+ * the gated residual above feeds two RMSNorm outputs that share one mean square, this layer's
+ * and the next layer's pre-norm:
+ *   residual_out = residual + sigmoid(gate) * x                                     (fp32)
+ *   out      = bf16_rne(residual_out * (mean(residual_out^2) + eps)^-1/2 * gamma)
+ *   out_next = bf16_rne(residual_out * (mean(residual_out^2) + eps)^-1/2 * gamma_next)
+ *  Arguments as for mf_gated_residual_rmsnorm, plus gamma_next bf16 [H] and out_next bf16 [T, H]
+ *  (16-byte aligned; out_next may overlap nothing).  residual_out and out are bit-identical to
+ *  what mf_gated_residual_rmsnorm returns for the same inputs.  Supported: as that function.
+ */
+int mf_gated_residual_next_rmsnorm(const uint16_t* x, const uint16_t* gate,
+                                   const float* residual, float* residual_out,
+                                   const uint16_t* gamma, const uint16_t* gamma_next, float eps,
+                                   uint16_t* out, uint16_t* out_next, int64_t T, int32_t H,
+                                   void* stream);
+
+/*
  * Per-head RMSNorm with a sigmoid gate ([PR6544] section 1.2; head dim 64):
  *   out[t,n,:] = bf16_rne(x[t,n,:] * (mean(x[t,n,:]^2) + eps)^-1/2 * gamma * sigmoid(gate[t,n,:]))
  *  x, gate, out bf16 [T, num_heads, head_dim]; gamma bf16 [head_dim], shared by all heads.
@@ -152,6 +171,7 @@ int64_t mf_moe_route_workspace_bytes(int64_t T, int32_t num_experts, int32_t k);
  */
 int mf_moe_finalize_supported(int32_t H, int32_t k, int per_expert);
 int mf_gated_residual_rmsnorm_supported(int32_t H);
+int mf_gated_residual_next_rmsnorm_supported(int32_t H);
 int mf_rmsnorm_sigmoid_gate_supported(int32_t head_dim);
 int mf_moe_route_supported(int32_t num_experts, int32_t k);
 

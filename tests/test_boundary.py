@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     L = ctypes.CDLL(mf.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -52,6 +52,8 @@ def test_supported_queries():
     assert not mf.mf_moe_finalize_supported(1024, 65)
     assert mf.mf_gated_residual_rmsnorm_supported(8192)
     assert not mf.mf_gated_residual_rmsnorm_supported(8190)
+    assert mf.mf_gated_residual_next_rmsnorm_supported(8192)
+    assert not mf.mf_gated_residual_next_rmsnorm_supported(32776)
     assert mf.mf_rmsnorm_sigmoid_gate_supported(64)
     assert not mf.mf_rmsnorm_sigmoid_gate_supported(128)
     assert mf.mf_moe_route_supported(256, 8)
@@ -111,6 +113,27 @@ def gated(x=A, gate=B, res=C, res_out=D, gamma=E_, eps=1e-6, out=F, T=8, H=8192)
 def test_gated_rejects_bad_arguments(kw, code):
     assert gated(**kw) == code
     assert gated(T=0) == OK
+
+
+H_ = 0x7F0700000000
+
+
+def gated_next(x=A, gate=B, res=C, res_out=D, gamma=E_, gnext=H_, eps=1e-6, out=F, onext=G,
+               T=8, H=8192):
+    return mf.lib().mf_gated_residual_next_rmsnorm(x, gate, res, res_out, gamma, gnext, eps, out,
+                                                   onext, T, H, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), SHAPE), (dict(H=8196), UNSUP), (dict(gnext=None), NULL), (dict(onext=None), NULL),
+    (dict(x=None), NULL), (dict(out=None), NULL), (dict(eps=float("nan")), VALUE),
+    (dict(gnext=H_ + 8), ALIGN), (dict(onext=G + 2), ALIGN), (dict(onext=F + 64), ALIAS),
+    (dict(onext=A), ALIAS), (dict(onext=D + 16), ALIAS), (dict(onext=H_), ALIAS),
+    (dict(res_out=H_), ALIAS), (dict(out=C + 16), ALIAS),
+])
+def test_gated_next_rejects_bad_arguments(kw, code):
+    assert gated_next(**kw) == code
+    assert gated_next(T=0) == OK
 
 
 def per_head(x=A, gate=B, gamma=C, eps=1e-6, out=D, T=4, heads=64, dim=64):

@@ -303,6 +303,63 @@ def test_gated_in_place():
     assert torch.equal(res, r2) and torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
+# ----------------------------------------------------------------------------- gated, dual output
+
+
+def gated_next_gpu(d, residual_out=None):
+    return mf.mf_gated_residual_next_rmsnorm(
+        up(d["x"], True), up(d["gate"], True), up(d["residual"]), up(d["gamma"], True),
+        up(d["gamma_next"], True), d["eps"], residual_out=residual_out)
+
+
+def check_gated_next(d):
+    out, on, r = gated_next_gpu(d)
+    torch.cuda.synchronize()
+    r_ref, o_ref, on_ref = oracle.gated_residual_next_rmsnorm(
+        d["x"], d["gate"], d["residual"], d["gamma"], d["gamma_next"], d["eps"])
+    assert_fp32_tol(r.cpu().numpy(), r_ref)
+    assert_bf16_close_given_residual_tol(bits(out), o_ref, r_ref, d["gamma"], d["eps"])
+    assert_bf16_close_given_residual_tol(bits(on), on_ref, r_ref, d["gamma_next"], d["eps"])
+    return out, on, r
+
+
+def test_gated_next_workload_full_size():
+    d = workloads.make_inputs("gated_residual_next_rmsnorm")
+    say(f"gated next T=4096 H=8192: {shape_str(2, 4096, 8192)}")
+    check_gated_next(d)
+
+
+@pytest.mark.parametrize("T,H", [(1, 8), (3, 520), (5000, 1024), (7, 32768), (2049, 8192),
+                                 (9, 12288)])
+def test_gated_next_matches_oracle(T, H):
+    say(f"gated next T={T} H={H}: {shape_str(2, T, H)}")
+    check_gated_next(workloads.make_gated_inputs(T, H, seed=3100 + T + H, dual=True))
+
+
+def test_gated_next_first_output_is_the_single_output_form():
+    # the dual form's residual_out and out are bit-identical to mf_gated_residual_rmsnorm's
+    d = workloads.make_gated_inputs(333, 8192, seed=84, dual=True)
+    say("gated next vs gated: T=333 H=8192")
+    out, on, r = gated_next_gpu(d)
+    out1, r1 = gated_gpu(d)
+    torch.cuda.synchronize()
+    assert torch.equal(r, r1) and torch.equal(out.view(torch.int16), out1.view(torch.int16))
+
+
+def test_gated_next_equal_gammas_and_in_place():
+    d = workloads.make_gated_inputs(100, 8192, seed=85, dual=True)
+    d["gamma_next"] = d["gamma"]
+    say("gated next: gamma_next == gamma, in place, T=100 H=8192")
+    res = up(d["residual"])
+    out, on, r = mf.mf_gated_residual_next_rmsnorm(
+        up(d["x"], True), up(d["gate"], True), res, up(d["gamma"], True), up(d["gamma"], True),
+        d["eps"], residual_out=res)
+    out2, on2, r2 = gated_next_gpu(d)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), on.view(torch.int16))
+    assert torch.equal(res, r2) and torch.equal(on.view(torch.int16), on2.view(torch.int16))
+
+
 # ----------------------------------------------------------------------------- per-head
 
 
