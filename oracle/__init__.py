@@ -1,6 +1,6 @@
-"""CPU oracle for the MoE finalize path, the sibling fused norms (gated residual RMSNorm, its
-dual-output "next" form, per-head RMSNorm with a sigmoid gate), and the routing and
-expert-sorted permutation the finalize consumes.
+"""CPU oracle for the MoE finalize path (and its expert-parallel partial and combine steps), the
+sibling fused norms (gated residual RMSNorm, its dual-output "next" form, per-head RMSNorm with
+a sigmoid gate), and the routing and expert-sorted permutation the finalize consumes.
 
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg
 of ``bench.py`` are the only callers.  The product path never imports this package, and
@@ -45,6 +45,8 @@ def _load():
         p, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
         lib.oracle_moe_finalize.argtypes = [p, i64, p, p, p, p, i32, p, p, p, f32, p, i64, i32, i32]
         lib.oracle_gated_residual_rmsnorm.argtypes = [p, p, p, p, p, f32, p, i64, i32]
+        lib.oracle_moe_finalize_ep_partial.argtypes = [p, i64, p, p, p, p, i32, f32, p, i64, i32, i32]
+        lib.oracle_moe_finalize_ep_combine.argtypes = [p, i32, p, p, p, f32, p, i64, i32]
         lib.oracle_gated_residual_next_rmsnorm.argtypes = [p, p, p, p, p, p, f32, p, p, i64, i32]
         lib.oracle_rmsnorm_sigmoid_gate.argtypes = [p, p, p, f32, p, i64, i32, i32]
         lib.oracle_moe_route.argtypes = [p, i64, i32, i32, p, p, p, p, p]
@@ -90,6 +92,50 @@ def moe_finalize(expert_rows, idx, weights, residual, gamma, eps, expert_ids=Non
                                  out.ctypes.data_as(ctypes.c_void_p), T, H, k)
     if st != 0:
         raise ValueError(f"oracle_moe_finalize failed with status {st}")
+    return r_out, out
+
+
+def moe_finalize_ep_partial(expert_rows, idx, weights, eps=1e-6, expert_ids=None,
+                            expert_gamma=None):
+    """This GPU's partial of the expert-parallel finalize: float32 [T, H].
+
+    Slots with idx < 0 belong to another GPU's experts and are skipped; the others are
+    accumulated as in moe_finalize (per-expert normalised when expert_gamma is given).
+    """
+    lib = _load()
+    rows, prows = _c(expert_rows, np.uint16)
+    idx, pidx = _c(idx, np.int32)
+    w, pw = _c(weights, np.float32)
+    T, k = idx.shape
+    H = rows.shape[1]
+    if (expert_ids is None) != (expert_gamma is None):
+        raise ValueError("expert_ids and expert_gamma go together")
+    pe = pge = None
+    E = 0
+    if expert_gamma is not None:
+        eids, pe = _c(expert_ids, np.int32)
+        ge, pge = _c(expert_gamma, np.uint16)
+        E = ge.shape[0]
+    part = np.empty((T, H), dtype=np.float32)
+    st = lib.oracle_moe_finalize_ep_partial(prows, rows.shape[0], pidx, pw, pe, pge, E, float(eps),
+                                            part.ctypes.data_as(ctypes.c_void_p), T, H, k)
+    if st != 0:
+        raise ValueError(f"oracle_moe_finalize_ep_partial failed with status {st}")
+    return part
+
+
+def moe_finalize_ep_combine(partials, residual, gamma, eps):
+    """The owner's combine: partials float32 [G, T, H] added in rank order, then the residual
+    add and RMSNorm.  Returns (residual_out float32 [T,H], out bf16-bits [T,H])."""
+    lib = _load()
+    parts, pp = _c(partials, np.float32)
+    res, pres = _c(residual, np.float32)
+    g, pg = _c(gamma, np.uint16)
+    G, T, H = parts.shape
+    r_out = np.empty((T, H), dtype=np.float32)
+    out = np.empty((T, H), dtype=np.uint16)
+    lib.oracle_moe_finalize_ep_combine(pp, G, pres, r_out.ctypes.data_as(ctypes.c_void_p), pg,
+                                       float(eps), out.ctypes.data_as(ctypes.c_void_p), T, H)
     return r_out, out
 
 

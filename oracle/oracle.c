@@ -1,5 +1,6 @@
 /*
- * Plain CPU oracle for the MoE finalize path, its sibling fused norms (gated residual
+ * Plain CPU oracle for the MoE finalize path (and its expert-parallel split into a partial
+ * sum per GPU and a combine on the token's owner), its sibling fused norms (gated residual
  * RMSNorm, the dual-output gated residual norm, per-head RMSNorm with a sigmoid gate), and the
  * routing that produces the finalize's gather indices and weights.
  *
@@ -146,6 +147,89 @@ done:
     free(acc);
     free(row);
     return status;
+}
+
+/*
+ * The MoE finalize split for expert parallelism (page "FlashInfer: fused norms and TP/EP MoE
+ * for Muse-Spark-Open", PR #6544, section 2.4: finalize + RMSNorm + all-reduce, where the
+ * slots of non-local experts skip the per-expert normalisation; page "MoE all-reduce fusion
+ * for Blackwell: FlashInfer's Cake backend", PR #4730, section 2: the all-reduce's sum of the
+ * expert outputs is fused with the residual add and RMSNorm).  Two steps:
+ *
+ *  ep_partial (on every GPU, over its local slots): idx[t,j] < 0 marks a slot whose expert
+ *  lives on another GPU; it is skipped entirely (no row read, no normalisation, no FMA).
+ *      partial[t,:] = +0; for j ascending with idx[t,j] >= 0:
+ *          partial = fmaf(w[t,j], row_j (per-expert normalised as in the finalize), partial)
+ *
+ *  ep_combine (on the token's owner, after the exchange): the G ranks' partials of a token
+ *  are added in ascending rank order from +0 (fixed order, so the result is deterministic),
+ *  then the residual add and the final RMSNorm exactly as in the finalize:
+ *      acc = +0; for g = 0..G-1: acc = acc + partials[g][t,:]        (float32 adds)
+ *      residual_out = residual + acc;  out = bf16(residual_out * rms_scale * gamma)
+ * With one rank holding every expert, the two steps give exactly the finalize's results.
+ */
+int oracle_moe_finalize_ep_partial(const uint16_t* expert_rows, int64_t num_rows,
+                                   const int32_t* idx, const float* weights,
+                                   const int32_t* expert_ids, const uint16_t* expert_gamma,
+                                   int32_t num_experts, float eps, float* partial, int64_t T,
+                                   int32_t H, int32_t k) {
+    float* row = (float*)malloc(sizeof(float) * (size_t)(H > 0 ? H : 1));
+    if (!row) return -2;
+    int status = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        float* acc = partial + t * (int64_t)H;
+        for (int32_t h = 0; h < H; ++h) acc[h] = 0.0f;
+        for (int32_t j = 0; j < k; ++j) {
+            int64_t p = idx[t * k + j];
+            if (p < 0) continue; /* another GPU's expert */
+            if (p >= num_rows) {
+                status = -1;
+                goto done;
+            }
+            const uint16_t* x = expert_rows + p * (int64_t)H;
+            if (expert_gamma) {
+                int32_t e = expert_ids[t * k + j];
+                if (e < 0 || e >= num_experts) {
+                    status = -1;
+                    goto done;
+                }
+                const uint16_t* ge = expert_gamma + (int64_t)e * H;
+                double s = rms_scale_bf16(x, H, eps);
+                for (int32_t h = 0; h < H; ++h)
+                    row[h] = (float)(bf16_value(x[h]) * s * bf16_value(ge[h]));
+            } else {
+                for (int32_t h = 0; h < H; ++h) row[h] = (float)bf16_value(x[h]);
+            }
+            float wj = weights[t * k + j];
+            for (int32_t h = 0; h < H; ++h) acc[h] = fmaf(wj, row[h], acc[h]);
+        }
+    }
+done:
+    free(row);
+    return status;
+}
+
+int oracle_moe_finalize_ep_combine(const float* partials, int32_t num_ranks,
+                                   const float* residual, float* residual_out,
+                                   const uint16_t* gamma, float eps, uint16_t* out, int64_t T,
+                                   int32_t H) {
+    float* acc = (float*)malloc(sizeof(float) * (size_t)(H > 0 ? H : 1));
+    if (!acc) return -2;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < H; ++h) acc[h] = 0.0f;
+        for (int32_t g = 0; g < num_ranks; ++g) {
+            const float* pg = partials + ((int64_t)g * T + t) * (int64_t)H;
+            for (int32_t h = 0; h < H; ++h) acc[h] = acc[h] + pg[h];
+        }
+        const float* res = residual + t * (int64_t)H;
+        float* r = residual_out + t * (int64_t)H;
+        for (int32_t h = 0; h < H; ++h) r[h] = res[h] + acc[h];
+        double s = rms_scale_f32(r, H, eps);
+        uint16_t* o = out + t * (int64_t)H;
+        for (int32_t h = 0; h < H; ++h) o[h] = bf16_round((double)r[h] * s * bf16_value(gamma[h]));
+    }
+    free(acc);
+    return 0;
 }
 
 /*

@@ -299,6 +299,98 @@ def test_per_expert_row_scale_invariance():
     assert np.array_equal(a, b)  # with eps = 0 the scale cancels exactly
 
 
+# ----------------------------------------------------------------------------- expert-parallel split
+
+
+def _ep_split(d, G):
+    """Per-rank idx arrays: expert e lives on rank e % G; other ranks' slots are -1."""
+    owner = d["expert_ids"] % G
+    return [np.where(owner == g, d["idx"], -1).astype(np.int32) for g in range(G)]
+
+
+@pytest.mark.parametrize("per_expert", [False, True])
+def test_ep_one_rank_is_the_finalize(per_expert):
+    d = workloads.make_finalize_inputs(9, 520, E=8, k=4, seed=40, per_expert=per_expert)
+    kw = dict(expert_ids=d["expert_ids"], expert_gamma=d["expert_gamma"]) if per_expert else {}
+    part = oracle.moe_finalize_ep_partial(d["expert_rows"], d["idx"], d["weights"], d["eps"], **kw)
+    r, o = oracle.moe_finalize_ep_combine(part[None], d["residual"], d["gamma"], d["eps"])
+    r_ref, o_ref = oracle.moe_finalize(d["expert_rows"], d["idx"], d["weights"], d["residual"],
+                                       d["gamma"], d["eps"], **kw)
+    assert np.array_equal(r, r_ref) and np.array_equal(o, o_ref)
+
+
+def test_ep_all_slots_remote_give_zero():
+    d = workloads.make_finalize_inputs(5, 64, E=8, k=3, seed=41)
+    part = oracle.moe_finalize_ep_partial(d["expert_rows"], np.full_like(d["idx"], -1),
+                                          d["weights"], d["eps"])
+    assert np.array_equal(part.view(np.uint32), np.zeros_like(part).view(np.uint32))  # +0
+
+
+@pytest.mark.parametrize("G", [2, 3, 8])
+def test_ep_exact_integers_match_the_finalize(G):
+    # small-integer rows, power-of-two weights, integer residual: every partial sum and every
+    # combine add is exact, so any rank split gives the single-GPU residual_out bit for bit
+    rng = np.random.default_rng(42 + G)
+    d = workloads.make_finalize_inputs(12, 256, E=16, k=6, seed=42 + G)
+    d["expert_rows"] = workloads.to_bf16_bits(rng.integers(-8, 9, d["expert_rows"].shape)
+                                              .astype(np.float32))
+    d["weights"] = (2.0 ** -rng.integers(0, 4, d["weights"].shape)).astype(np.float32)
+    d["residual"] = rng.integers(-16, 17, d["residual"].shape).astype(np.float32)
+    parts = np.stack([oracle.moe_finalize_ep_partial(d["expert_rows"], i, d["weights"], d["eps"])
+                      for i in _ep_split(d, G)])
+    r, o = oracle.moe_finalize_ep_combine(parts, d["residual"], d["gamma"], d["eps"])
+    closed = d["residual"].astype(np.float64) + (d["weights"][..., None].astype(np.float64) *
+                                                 f32(d["expert_rows"])[d["idx"]]).sum(axis=1)
+    assert np.array_equal(r, closed.astype(np.float32))
+    r_ref, o_ref = oracle.moe_finalize(d["expert_rows"], d["idx"], d["weights"], d["residual"],
+                                       d["gamma"], d["eps"])
+    assert np.array_equal(r, r_ref) and np.array_equal(o, o_ref)
+
+
+def test_ep_brute_force_partials_and_combine():
+    G = 4
+    d = workloads.make_finalize_inputs(10, 384, E=16, k=8, seed=43)
+    X = f32(d["expert_rows"]).astype(np.float64)
+    w = d["weights"].astype(np.float64)
+    parts = []
+    for g, ig in enumerate(_ep_split(d, G)):
+        p = oracle.moe_finalize_ep_partial(d["expert_rows"], ig, d["weights"], d["eps"])
+        local = (ig >= 0)[..., None]
+        terms = np.where(local, w[..., None] * X[np.maximum(ig, 0)], 0.0)
+        exact = terms.sum(axis=1)
+        assert np.all(np.abs(p - exact) <= 9 * U32 * 2 * np.abs(terms).sum(axis=1) + 1e-30), g
+        parts.append(p)
+    r, o = oracle.moe_finalize_ep_combine(np.stack(parts), d["residual"], d["gamma"], d["eps"])
+    terms = w[..., None] * X[d["idx"]]
+    exact = d["residual"].astype(np.float64) + terms.sum(axis=1)
+    bound = (8 + G + 2) * U32 * 2 * (np.abs(terms).sum(axis=1) + np.abs(d["residual"]))
+    assert np.all(np.abs(r - exact) <= bound)
+    assert _close_bf16(o, _rmsnorm_bits(r, d["gamma"], d["eps"]))
+
+
+def test_ep_combine_adds_ranks_in_ascending_order():
+    # partials 1, 2^-24, 2^-24 (ranks 0, 1, 2), residual 0: in rank order (0 + 1) + 2^-24 is a
+    # tie that rounds to even, 1, and so does the next add: residual_out is exactly 1.  The
+    # reverse order would give 2^-23 + 1 = 1 + 2^-23.
+    T, H = 2, 8
+    parts = np.stack([np.ones((T, H)), np.full((T, H), 2.0 ** -24), np.full((T, H), 2.0 ** -24)])
+    r, _ = oracle.moe_finalize_ep_combine(parts.astype(np.float32), np.zeros((T, H), np.float32),
+                                          workloads.to_bf16_bits(np.ones(H, np.float32)), 1e-6)
+    assert np.array_equal(r, np.ones((T, H), np.float32))
+
+
+def test_ep_remote_slots_skip_the_per_expert_norm():
+    # a remote slot's expert id and weight are never read: garbage there changes nothing
+    d = workloads.make_finalize_inputs(6, 256, E=8, k=4, seed=44, per_expert=True)
+    ig = _ep_split(d, 2)[0]
+    eids = np.where(ig >= 0, d["expert_ids"], 10 ** 6).astype(np.int32)
+    w = np.where(ig >= 0, d["weights"], np.nan).astype(np.float32)
+    p1 = oracle.moe_finalize_ep_partial(d["expert_rows"], ig, w, d["eps"], eids, d["expert_gamma"])
+    p2 = oracle.moe_finalize_ep_partial(d["expert_rows"], ig, d["weights"], d["eps"],
+                                        d["expert_ids"], d["expert_gamma"])
+    assert np.array_equal(p1, p2)
+
+
 # ----------------------------------------------------------------------------- gated
 
 
