@@ -14,7 +14,7 @@ traffic: HBM bytes per launch measured with rocprofv3 counters, read from the co
 summary under profiles/ when it was taken from the current kernel sources, else null.
 cpu_baseline: the CPU oracle timed on a bounded sample of the same workload on the host.
 Other workloads (--workload) time the sibling kernels (the gated norms, single and dual output,
-and the per-head norm), the routing producer (one step = one
+and the per-head norm), the expert-parallel partial and combine steps, the routing producer (one step = one
 mf_moe_route call: its three kernels, timed together by the events around the call) and the
 copy used for calibration.
 """
@@ -46,6 +46,10 @@ _NORM_SOURCES = ["mf_device.h", "row_norm.h", "norm_kernels.h", "api_util.h", "r
 KERNEL_SOURCES = {
     "finalize": ["mf_device.h", "row_norm.h", "finalize_kernel.h", "api_util.h", "row_shape.h",
                  "mf_api.hip"],
+    "ep_partial": ["mf_device.h", "row_norm.h", "finalize_kernel.h", "api_util.h", "row_shape.h",
+                   "mf_api.hip"],
+    "ep_combine": ["mf_device.h", "row_norm.h", "finalize_kernel.h", "api_util.h", "row_shape.h",
+                   "mf_api.hip"],
     "gated": _NORM_SOURCES,
     "gated_next": _NORM_SOURCES,
     "per_head": _NORM_SOURCES,
@@ -93,6 +97,14 @@ def algorithmic_bytes(d: dict) -> int:
         if d.get("expert_gamma") is not None:
             b += T * k * 4 + len(np.unique(d["expert_ids"])) * H * 2
         return b
+    if kind == "ep_partial":
+        # local rows read, every idx read, local weights read, the fp32 partial written
+        T, H, k = d["T"], d["H"], d["k"]
+        local = int((d["idx"] >= 0).sum())
+        return local * (H * 2 + 4) + T * k * 4 + T * H * 4
+    if kind == "ep_combine":
+        T, H, G = d["T"], d["H"], d["G"]
+        return G * T * H * 4 + T * H * (4 + 4 + 2) + H * 2
     if kind == "gated":
         T, H = d["T"], d["H"]
         return T * H * (2 + 2 + 4 + 4 + 2) + H * 2
@@ -145,6 +157,15 @@ def upload(d: dict, dev):
                     gamma=up(d["gamma"], True),
                     res_out=torch.empty((T, H), dtype=torch.float32, device=dev),
                     out=torch.empty((T, H), dtype=torch.bfloat16, device=dev))
+    if kind == "ep_partial":
+        T, H = d["T"], d["H"]
+        return dict(rows=up(d["expert_rows"], True), idx=up(d["idx"]), w=up(d["weights"]),
+                    part=torch.empty((T, H), dtype=torch.float32, device=dev))
+    if kind == "ep_combine":
+        T, H = d["T"], d["H"]
+        return dict(parts=up(d["partials"]), res=up(d["residual"]), gamma=up(d["gamma"], True),
+                    res_out=torch.empty((T, H), dtype=torch.float32, device=dev),
+                    out=torch.empty((T, H), dtype=torch.bfloat16, device=dev))
     if kind == "gated_next":
         T, H = d["T"], d["H"]
         e = lambda dt: torch.empty((T, H), dtype=dt, device=dev)
@@ -183,6 +204,12 @@ def launcher(d: dict, g: dict):
         return lambda: mf.mf_gated_residual_rmsnorm(g["x"], g["gate"], g["res"], g["gamma"],
                                                     d["eps"], residual_out=g["res_out"],
                                                     out=g["out"])
+    if kind == "ep_partial":
+        return lambda: mf.mf_moe_finalize_ep_partial(g["rows"], g["idx"], g["w"], d["eps"],
+                                                     partial=g["part"])
+    if kind == "ep_combine":
+        return lambda: mf.mf_moe_finalize_ep_combine(g["parts"], g["res"], g["gamma"], d["eps"],
+                                                     residual_out=g["res_out"], out=g["out"])
     if kind == "gated_next":
         return lambda: mf.mf_gated_residual_next_rmsnorm(
             g["x"], g["gate"], g["res"], g["gamma"], g["gamma_next"], d["eps"],
@@ -202,10 +229,12 @@ def launcher(d: dict, g: dict):
 def launch_config(name: str, d: dict) -> dict:
     import finalize_residual_rmsnorm_amd as mf
     kind = d["kind"]
-    if kind == "finalize":
+    if kind in ("finalize", "ep_partial"):
         pe = d.get("expert_gamma") is not None
         return mf.mf_launch_shape(mf.KIND_FINALIZE_PER_EXPERT if pe else mf.KIND_FINALIZE,
                                   d["T"], d["H"], d["k"])
+    if kind == "ep_combine":
+        return mf.mf_launch_shape(mf.KIND_GATED, d["T"], d["H"])  # the same row shape
     if kind in ("gated", "gated_next"):
         return mf.mf_launch_shape(mf.KIND_GATED, d["T"], d["H"])
     return {}
@@ -241,6 +270,12 @@ def cpu_baseline(d: dict, target_cpu_s: float = 15.0, max_threads: int = 16) -> 
             oracle.rmsnorm_sigmoid_gate(d["x"][lo:hi], d["gate"][lo:hi], d["gamma"], d["eps"])
         elif kind == "route":
             oracle.moe_route(d["logits"][lo:hi], d["k"])
+        elif kind == "ep_partial":
+            oracle.moe_finalize_ep_partial(d["expert_rows"], d["idx"][lo:hi], d["weights"][lo:hi],
+                                           d["eps"])
+        elif kind == "ep_combine":
+            oracle.moe_finalize_ep_combine(d["partials"][:, lo:hi], d["residual"][lo:hi],
+                                           d["gamma"], d["eps"])
 
     T = d["T"]
     try:
@@ -284,7 +319,8 @@ def main() -> int:
     ap.add_argument("--workload", default="finalize_prefill",
                     choices=["finalize_prefill", "finalize_decode_per_expert", "finalize_tiny",
                              "gated_residual_rmsnorm", "gated_residual_next_rmsnorm",
-                             "rmsnorm_sigmoid_gate", "moe_route_prefill",
+                             "rmsnorm_sigmoid_gate", "moe_route_prefill", "finalize_ep_partial",
+                             "finalize_ep_combine",
                              "moe_route_decode", "stream_copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

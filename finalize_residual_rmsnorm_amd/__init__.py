@@ -21,7 +21,8 @@ __all__ = [
     "mf_moe_finalize_supported", "mf_gated_residual_rmsnorm_supported",
     "mf_rmsnorm_sigmoid_gate_supported", "mf_launch_shape", "mf_stream_copy", "mf_status_string",
     "mf_moe_route", "mf_moe_route_supported", "mf_moe_route_workspace_bytes",
-    "mf_gated_residual_next_rmsnorm", "mf_gated_residual_next_rmsnorm_supported", "LIB_PATH",
+    "mf_gated_residual_next_rmsnorm", "mf_gated_residual_next_rmsnorm_supported",
+    "mf_moe_finalize_ep_partial", "mf_moe_finalize_ep_combine", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmf.so")
@@ -61,6 +62,8 @@ def lib() -> ctypes.CDLL:
             "mf_moe_route": [p, i64, i32, i32, p, p, p, p, p, p, i64, p],
             "mf_gated_residual_next_rmsnorm": [p, p, p, p, p, p, f32, p, p, i64, i32, p],
             "mf_gated_residual_next_rmsnorm_supported": [i32],
+            "mf_moe_finalize_ep_partial": [p, i64, p, p, p, p, i32, f32, p, i64, i32, i32, p],
+            "mf_moe_finalize_ep_combine": [p, i32, p, p, p, f32, p, i64, i32, p],
             "mf_moe_route_supported": [i32, i32],
             "mf_moe_route_workspace_bytes": [i64, i32, i32],
         }
@@ -138,6 +141,55 @@ def mf_moe_finalize(expert_rows: torch.Tensor, idx: torch.Tensor, weights: torch
         _dev(gamma, torch.bfloat16, "gamma", (H,)), float(eps),
         _dev(out, torch.bfloat16, "out", (T, H)), T, H, k, _stream(stream, dev))
     _check("mf_moe_finalize", st)
+    return out, residual_out
+
+
+def mf_moe_finalize_ep_partial(expert_rows: torch.Tensor, idx: torch.Tensor,
+                               weights: torch.Tensor, eps: float = 1e-6, *,
+                               expert_ids: torch.Tensor | None = None,
+                               expert_gamma: torch.Tensor | None = None,
+                               partial: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """This GPU's partial of the expert-parallel finalize (fp32 [T, H]).  idx < 0 marks a slot
+    whose expert lives on another GPU: it is skipped."""
+    T, k = idx.shape
+    num_rows, H = expert_rows.shape
+    dev = expert_rows.device
+    if partial is None:
+        partial = torch.empty((T, H), dtype=torch.float32, device=dev)
+    pe = pg = None
+    E = 0
+    if (expert_ids is None) != (expert_gamma is None):
+        raise ValueError("expert_ids and expert_gamma go together")
+    if expert_gamma is not None:
+        E = expert_gamma.shape[0]
+        pe = _dev(expert_ids, torch.int32, "expert_ids", (T, k))
+        pg = _dev(expert_gamma, torch.bfloat16, "expert_gamma", (E, H))
+    st = lib().mf_moe_finalize_ep_partial(
+        _dev(expert_rows, torch.bfloat16, "expert_rows"), num_rows, _dev(idx, torch.int32, "idx"),
+        _dev(weights, torch.float32, "weights", (T, k)), pe, pg, E, float(eps),
+        _dev(partial, torch.float32, "partial", (T, H)), T, H, k, _stream(stream, dev))
+    _check("mf_moe_finalize_ep_partial", st)
+    return partial
+
+
+def mf_moe_finalize_ep_combine(partials: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor,
+                               eps: float = 1e-6, *, residual_out: torch.Tensor | None = None,
+                               out: torch.Tensor | None = None, stream=None):
+    """The token owner's combine: partials fp32 [G, T, H] added in rank order, then the
+    residual add and RMSNorm.  Returns (out bf16 [T,H], residual_out fp32 [T,H])."""
+    G, T, H = partials.shape
+    dev = partials.device
+    if residual_out is None:
+        residual_out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    st = lib().mf_moe_finalize_ep_combine(
+        _dev(partials, torch.float32, "partials"), G,
+        _dev(residual, torch.float32, "residual", (T, H)),
+        _dev(residual_out, torch.float32, "residual_out", (T, H)),
+        _dev(gamma, torch.bfloat16, "gamma", (H,)), float(eps),
+        _dev(out, torch.bfloat16, "out", (T, H)), T, H, _stream(stream, dev))
+    _check("mf_moe_finalize_ep_combine", st)
     return out, residual_out
 
 

@@ -20,6 +20,16 @@
 //  - No MFMA: the arithmetic intensity is below 1 flop per byte; the kernel is bound by HBM.
 //  - No atomics and a fixed reduction order: results are bit-deterministic and identical for
 //    a token whatever batch it is in.
+//
+// Expert-parallel split (PR #6544 page, section 2.4: finalize + RMSNorm + all-reduce, the
+// slots of non-local experts skipping normalisation; PR #4730 page, section 2: the
+// all-reduce's sum fused with the residual add and RMSNorm):
+//  - PARTIAL mode of moe_finalize_kernel: one GPU's share.  idx < 0 marks a slot whose expert
+//    lives on another GPU; it is skipped (no row read, no norm, no FMA; the test is on a
+//    wave-uniform scalar, so it is a branch, not a mask).  The fp32 accumulator is stored as
+//    the token's partial; no residual, no norm.
+//  - moe_finalize_combine_kernel: the token owner adds the ranks' partials in ascending rank
+//    order from +0, then the residual add and the final RMSNorm as above.
 #pragma once
 
 #include "row_norm.h"
@@ -62,15 +72,17 @@ constexpr int finalize_min_waves(int vpl, bool per_expert) {
     return per_expert ? 2 : (vpl == 1 ? 8 : 4);
 }
 
-// One gather batch: JB rows (and, per-expert, their gamma rows) of the lane's slots.
-template <int VPL, int JB, bool PER_EXPERT>
+// One gather batch: JB rows (and, per-expert, their gamma rows) of the lane's slots; with
+// SKIP, which of them are local (live).
+template <int VPL, int JB, bool PER_EXPERT, bool SKIP = false>
 struct GatherBatch {
     u32x4 x[JB][VPL];
     u32x4 g[PER_EXPERT ? JB : 1][VPL];
+    bool live[SKIP ? JB : 1];
 };
 
-template <int VPL, int JB, bool PER_EXPERT, int TAIL>
-__device__ __forceinline__ void issue_batch(GatherBatch<VPL, JB, PER_EXPERT>& b,
+template <int VPL, int JB, bool PER_EXPERT, int TAIL, bool SKIP>
+__device__ __forceinline__ void issue_batch(GatherBatch<VPL, JB, PER_EXPERT, SKIP>& b,
                                             const FinalizeArgs& a, int64_t tk, int jb, int k,
                                             const Slots<VPL, TAIL>& sl) {
     const int64_t last_row = a.num_rows - 1;
@@ -79,6 +91,19 @@ __device__ __forceinline__ void issue_batch(GatherBatch<VPL, JB, PER_EXPERT>& b,
         // Past the last j of a partial batch, reload row k-1 (same cache lines; unused).
         const int j = min(jb + u, k - 1);
         int64_t row = a.idx[tk + j];
+        if constexpr (SKIP) {
+            // another GPU's expert: nothing is read for it (a wave-uniform branch)
+            b.live[u] = row >= 0;
+            if (row < 0) {
+#pragma unroll
+                for (int s = 0; s < VPL; ++s) b.x[u][s] = u32x4{0u, 0u, 0u, 0u};
+                if constexpr (PER_EXPERT) {
+#pragma unroll
+                    for (int s = 0; s < VPL; ++s) b.g[u][s] = u32x4{0u, 0u, 0u, 0u};
+                }
+                continue;
+            }
+        }
         row = row < 0 ? 0 : (row > last_row ? last_row : row);
         const uint16_t* rp = a.rows + row * a.H;
 #pragma unroll
@@ -96,8 +121,8 @@ __device__ __forceinline__ void issue_batch(GatherBatch<VPL, JB, PER_EXPERT>& b,
 
 // acc += w_j * row_j for the batch's rows in ascending j (per-expert: row_j normalised with
 // its own mean square and multiplied by its expert's gamma first).
-template <int VPL, int JB, bool PER_EXPERT, int TAIL>
-__device__ __forceinline__ void consume_batch(const GatherBatch<VPL, JB, PER_EXPERT>& b,
+template <int VPL, int JB, bool PER_EXPERT, int TAIL, bool SKIP>
+__device__ __forceinline__ void consume_batch(const GatherBatch<VPL, JB, PER_EXPERT, SKIP>& b,
                                               float (&acc)[VPL][8], const FinalizeArgs& a,
                                               int64_t tk, int jb, int k,
                                               const Slots<VPL, TAIL>& sl, TokenLds& L,
@@ -117,7 +142,9 @@ __device__ __forceinline__ void consume_batch(const GatherBatch<VPL, JB, PER_EXP
     }
 #pragma unroll
     for (int u = 0; u < JB; ++u) {
-        if (jb + u < k) {
+        bool use = jb + u < k;
+        if constexpr (SKIP) use = use && b.live[u];
+        if (use) {
             const float wj = a.w[tk + jb + u];
 #pragma unroll
             for (int s = 0; s < VPL; ++s) {
@@ -138,8 +165,10 @@ __device__ __forceinline__ void consume_batch(const GatherBatch<VPL, JB, PER_EXP
     }
 }
 
-// KC: the top-k fixed at compile time (8), or 0 for a runtime k.
-template <int VPL, int KC, bool PER_EXPERT, int TAIL>
+// KC: the top-k fixed at compile time (8), or 0 for a runtime k.  PARTIAL: this GPU's share
+// of the expert-parallel split (slots with idx < 0 skipped; the fp32 accumulator is stored to
+// residual_out, which then holds the [T, H] partial; residual, gamma and out are unused).
+template <int VPL, int KC, bool PER_EXPERT, int TAIL, bool PARTIAL = false>
 __global__ void __launch_bounds__(finalize_block_max(PER_EXPERT))
 __attribute__((amdgpu_waves_per_eu(finalize_min_waves(VPL, PER_EXPERT), 8)))
 moe_finalize_kernel(const FinalizeArgs a) {
@@ -175,10 +204,14 @@ moe_finalize_kernel(const FinalizeArgs a) {
     constexpr int UNROLL = KC > 0 ? (KC + JB - 1) / JB : 1;
 #pragma unroll UNROLL
     for (int jb = 0; jb < k; jb += JB) {
-        GatherBatch<VPL, JB, PER_EXPERT> b;
+        GatherBatch<VPL, JB, PER_EXPERT, PARTIAL> b;
         issue_batch(b, a, tk, jb, k, sl);
-        if (EARLY && jb == 0) load_res_gamma();
+        if (!PARTIAL && EARLY && jb == 0) load_res_gamma();
         consume_batch(b, acc, a, tk, jb, k, sl, L, m);
+    }
+    if constexpr (PARTIAL) {
+        store_residual(acc, sl, a.residual_out + m.t * H);  // the token's partial
+        return;
     }
     if (!EARLY) load_res_gamma();
 
@@ -194,6 +227,94 @@ moe_finalize_kernel(const FinalizeArgs a) {
         }
     store_residual(acc, sl, a.residual_out + m.t * H);
     rmsnorm_store(acc, g, sl, a.out + m.t * H, H, a.eps, L, m);
+}
+
+// The token owner's combine of the expert-parallel split.
+struct CombineArgs {
+    const float* partials;   // [G, T, H]: rank g's partial of token t at (g*T + t)*H
+    const float* residual;   // [T, H]
+    float* residual_out;     // [T, H], may equal residual
+    const uint16_t* gamma;   // bf16 [H]
+    uint16_t* out;           // bf16 [T, H]
+    int64_t T;
+    int32_t H;
+    int32_t G;
+    float eps;
+};
+
+// Ranks whose partial rows are in flight together: 32 fp32 values per lane, so that two
+// 16-wave workgroups fit on a CU at one slot per wave.
+constexpr int combine_batch(int vpl) { return vpl == 1 ? 4 : (vpl == 2 ? 2 : 1); }
+
+template <int VPL, int TAIL>
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(VPL == 1 ? 8 : 4, 8)))
+moe_finalize_combine_kernel(const CombineArgs a) {
+    constexpr int kCombineBatch = combine_batch(VPL);
+    extern __shared__ float lds[];
+    const RowMap m = row_map();
+    const int H = a.H;
+    const Slots<VPL, TAIL> sl = slot_offsets<VPL, TAIL>(m, H);
+    const int64_t row = m.t * H;
+    const int64_t rank_stride = a.T * H;
+
+    float acc[VPL][8];
+#pragma unroll
+    for (int s = 0; s < VPL; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[s][i] = 0.0f;
+    f32x4 rv[VPL][2];
+    u32x4 g[VPL];
+    auto load_res_gamma = [&]() {
+#pragma unroll
+        for (int s = 0; s < VPL; ++s) {
+            rv[s][0] = ld_stream(at<f32x4>(a.residual + row, sl.eoff[s] * 4u));
+            rv[s][1] = ld_stream(at<f32x4>(a.residual + row, sl.eoff[s] * 4u + 16u));
+        }
+        load_gamma(g, a.gamma, sl);
+    };
+    // With small row slices the residual and gamma ride along with the first batch.
+    constexpr bool EARLY = VPL <= 2;
+    for (int g0 = 0; g0 < a.G; g0 += kCombineBatch) {
+        f32x4 p[kCombineBatch][VPL][2];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            // past the last rank of a partial batch, reload rank G-1 (unused)
+            const int gr = g0 + u < a.G ? g0 + u : a.G - 1;
+            const float* pr = a.partials + gr * rank_stride + row;
+#pragma unroll
+            for (int s = 0; s < VPL; ++s) {
+                // spare waves past the row skip their loads
+                p[u][s][0] = sl.suni[s] ? ld_stream(at<f32x4>(pr, sl.eoff[s] * 4u)) : f32x4{0.f, 0.f, 0.f, 0.f};
+                p[u][s][1] = sl.suni[s] ? ld_stream(at<f32x4>(pr, sl.eoff[s] * 4u + 16u)) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        if (EARLY && g0 == 0) load_res_gamma();
+        // ascending rank order: acc = acc + partial_g
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            if (g0 + u < a.G) {
+#pragma unroll
+                for (int s = 0; s < VPL; ++s)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[s][i] = acc[s][i] + p[u][s][0][i];
+                        acc[s][4 + i] = acc[s][4 + i] + p[u][s][1][i];
+                    }
+            }
+        }
+    }
+    if (!EARLY) load_res_gamma();
+    // residual add, then the store (every residual load precedes it: in-place is safe)
+#pragma unroll
+    for (int s = 0; s < VPL; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[s][i] = rv[s][0][i] + acc[s][i];
+            acc[s][4 + i] = rv[s][1][i] + acc[s][4 + i];
+        }
+    store_residual(acc, sl, a.residual_out + row);
+    TokenLds L = token_lds(lds, m.wpt, 1);
+    rmsnorm_store(acc, g, sl, a.out + row, H, a.eps, L, m);
 }
 
 }  // namespace mf

@@ -36,12 +36,12 @@ RowShape finalize_shape(int64_t T, int32_t H, int32_t k, bool per_expert) {
     return s;
 }
 
-template <int VPL, int KC, bool PE>
+template <int VPL, int KC, bool PE, bool PARTIAL>
 const void* finalize_fn(int tail) {
     switch (tail) {
-        case kRowFull: return reinterpret_cast<const void*>(&moe_finalize_kernel<VPL, KC, PE, kRowFull>);
-        case kRowWhole: return reinterpret_cast<const void*>(&moe_finalize_kernel<VPL, KC, PE, kRowWhole>);
-        default: return reinterpret_cast<const void*>(&moe_finalize_kernel<VPL, KC, PE, kRowRagged>);
+        case kRowFull: return reinterpret_cast<const void*>(&moe_finalize_kernel<VPL, KC, PE, kRowFull, PARTIAL>);
+        case kRowWhole: return reinterpret_cast<const void*>(&moe_finalize_kernel<VPL, KC, PE, kRowWhole, PARTIAL>);
+        default: return reinterpret_cast<const void*>(&moe_finalize_kernel<VPL, KC, PE, kRowRagged, PARTIAL>);
     }
 }
 
@@ -50,36 +50,63 @@ const void* finalize_fn(int tail) {
 // gathered row).  Wider slices keep the batched loop.
 constexpr bool uses_compiled_topk(int vpl, bool per_expert) { return vpl <= (per_expert ? 1 : 2); }
 
-template <int VPL, bool PE>
+template <int VPL, bool PE, bool PARTIAL>
 const void* finalize_fn(int tail, int k) {
     if constexpr (uses_compiled_topk(VPL, PE)) {
-        if (k == kCompiledTopK) return finalize_fn<VPL, kCompiledTopK, PE>(tail);
+        if (k == kCompiledTopK) return finalize_fn<VPL, kCompiledTopK, PE, PARTIAL>(tail);
     }
-    return finalize_fn<VPL, 0, PE>(tail);
+    return finalize_fn<VPL, 0, PE, PARTIAL>(tail);
 }
 
-const void* finalize_kernel_for(const RowShape& s, int k, bool per_expert) {
+template <bool PARTIAL>
+const void* finalize_kernel_for_mode(const RowShape& s, int k, bool per_expert) {
     if (per_expert) {
         switch (s.vpl) {
-            case 1: return finalize_fn<1, true>(s.tail, k);
-            case 2: return finalize_fn<2, true>(s.tail, k);
-            case 3: return finalize_fn<3, true>(s.tail, k);
-            case 4: return finalize_fn<4, true>(s.tail, k);
-            case 5: return finalize_fn<5, true>(s.tail, k);
-            case 6: return finalize_fn<6, true>(s.tail, k);
-            case 7: return finalize_fn<7, true>(s.tail, k);
-            case 8: return finalize_fn<8, true>(s.tail, k);
+            case 1: return finalize_fn<1, true, PARTIAL>(s.tail, k);
+            case 2: return finalize_fn<2, true, PARTIAL>(s.tail, k);
+            case 3: return finalize_fn<3, true, PARTIAL>(s.tail, k);
+            case 4: return finalize_fn<4, true, PARTIAL>(s.tail, k);
+            case 5: return finalize_fn<5, true, PARTIAL>(s.tail, k);
+            case 6: return finalize_fn<6, true, PARTIAL>(s.tail, k);
+            case 7: return finalize_fn<7, true, PARTIAL>(s.tail, k);
+            case 8: return finalize_fn<8, true, PARTIAL>(s.tail, k);
             default: return nullptr;
         }
     }
     switch (s.vpl) {
-        case 1: return finalize_fn<1, false>(s.tail, k);
-        case 2: return finalize_fn<2, false>(s.tail, k);
-        case 3: return finalize_fn<3, false>(s.tail, k);
-        case 4: return finalize_fn<4, false>(s.tail, k);
+        case 1: return finalize_fn<1, false, PARTIAL>(s.tail, k);
+        case 2: return finalize_fn<2, false, PARTIAL>(s.tail, k);
+        case 3: return finalize_fn<3, false, PARTIAL>(s.tail, k);
+        case 4: return finalize_fn<4, false, PARTIAL>(s.tail, k);
         default: return nullptr;
     }
 }
+
+const void* finalize_kernel_for(const RowShape& s, int k, bool per_expert, bool partial = false) {
+    return partial ? finalize_kernel_for_mode<true>(s, k, per_expert)
+                   : finalize_kernel_for_mode<false>(s, k, per_expert);
+}
+
+template <int VPL>
+const void* combine_fn(int tail) {
+    switch (tail) {
+        case kRowFull: return reinterpret_cast<const void*>(&moe_finalize_combine_kernel<VPL, kRowFull>);
+        case kRowWhole: return reinterpret_cast<const void*>(&moe_finalize_combine_kernel<VPL, kRowWhole>);
+        default: return reinterpret_cast<const void*>(&moe_finalize_combine_kernel<VPL, kRowRagged>);
+    }
+}
+
+const void* combine_kernel_for(const RowShape& s) {
+    switch (s.vpl) {
+        case 1: return combine_fn<1>(s.tail);
+        case 2: return combine_fn<2>(s.tail);
+        case 3: return combine_fn<3>(s.tail);
+        case 4: return combine_fn<4>(s.tail);
+        default: return nullptr;
+    }
+}
+
+constexpr int32_t kMaxRanks = 1024;
 
 }  // namespace
 
@@ -162,6 +189,99 @@ int mf_moe_finalize(const uint16_t* expert_rows, int64_t num_rows, const int32_t
     a.H = H;
     a.k = k;
     a.num_experts = per_expert ? num_experts : 0;
+    a.eps = eps;
+    void* args[] = {&a};
+    return hip_status(hipLaunchKernel(fn, dim3((unsigned)s.grid), dim3(s.block), args, s.lds,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+int mf_moe_finalize_ep_partial(const uint16_t* expert_rows, int64_t num_rows,
+                               const int32_t* idx, const float* weights,
+                               const int32_t* expert_ids, const uint16_t* expert_gamma,
+                               int32_t num_experts, float eps, float* partial, int64_t T,
+                               int32_t H, int32_t k, void* stream) {
+    if (T < 0 || num_rows < 0) return MF_ERR_SHAPE;
+    const bool per_expert = expert_ids != nullptr || expert_gamma != nullptr;
+    if (!mf_moe_finalize_supported(H, k, per_expert)) return MF_ERR_UNSUPPORTED;
+    if (T == 0) return MF_OK;
+    const RowShape s = finalize_shape(T, H, k, per_expert);
+    if (!grid_fits(s.grid, s.block)) return MF_ERR_SHAPE;
+    const void* fn = finalize_kernel_for(s, k, per_expert, true);
+    if (!fn || s.block > finalize_block_max(per_expert)) return MF_ERR_UNSUPPORTED;
+    if (!expert_rows || !idx || !weights || !partial) return MF_ERR_NULL;
+    if (per_expert && (!expert_ids || !expert_gamma)) return MF_ERR_NULL;
+    if (num_rows < 1 || (per_expert && num_experts < 1)) return MF_ERR_SHAPE;
+    if (!eps_ok(eps)) return MF_ERR_VALUE;
+    if (!aligned(expert_rows, 16) || !aligned(partial, 16) || !aligned(idx, 4) ||
+        !aligned(weights, 4) ||
+        (per_expert && (!aligned(expert_gamma, 16) || !aligned(expert_ids, 4))))
+        return MF_ERR_ALIGN;
+    const size_t th = size_t(T) * H;
+    const size_t tk = size_t(T) * k;
+    const void* ins[] = {expert_rows, idx, weights, expert_ids, expert_gamma};
+    const size_t in_bytes[] = {size_t(num_rows) * H * 2, tk * 4, tk * 4, per_expert ? tk * 4 : 0,
+                               per_expert ? size_t(num_experts) * H * 2 : 0};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(partial, th * 4, ins[i], in_bytes[i])) return MF_ERR_ALIAS;
+
+    FinalizeArgs a;
+    a.rows = expert_rows;
+    a.idx = idx;
+    a.w = weights;
+    a.eids = expert_ids;
+    a.egamma = expert_gamma;
+    a.residual = nullptr;
+    a.residual_out = partial;
+    a.gamma = nullptr;
+    a.out = nullptr;
+    a.T = T;
+    a.num_rows = num_rows;
+    a.H = H;
+    a.k = k;
+    a.num_experts = per_expert ? num_experts : 0;
+    a.eps = eps;
+    void* args[] = {&a};
+    return hip_status(hipLaunchKernel(fn, dim3((unsigned)s.grid), dim3(s.block), args, s.lds,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+int mf_moe_finalize_ep_combine(const float* partials, int32_t num_ranks, const float* residual,
+                               float* residual_out, const uint16_t* gamma, float eps,
+                               uint16_t* out, int64_t T, int32_t H, void* stream) {
+    if (T < 0 || num_ranks < 1 || num_ranks > kMaxRanks) return MF_ERR_SHAPE;
+    if (!row_width_supported(H)) return MF_ERR_UNSUPPORTED;
+    if (T == 0) return MF_OK;
+    const RowShape s = row_shape(T, H, kMaxWaves, kMaxVpl);
+    if (!grid_fits(s.grid, s.block)) return MF_ERR_SHAPE;
+    const void* fn = combine_kernel_for(s);
+    if (!fn) return MF_ERR_UNSUPPORTED;
+    if (!partials || !residual || !residual_out || !gamma || !out) return MF_ERR_NULL;
+    if (!eps_ok(eps)) return MF_ERR_VALUE;
+    if (!aligned(partials, 16) || !aligned(residual, 16) || !aligned(residual_out, 16) ||
+        !aligned(gamma, 16) || !aligned(out, 16))
+        return MF_ERR_ALIGN;
+    const size_t th = size_t(T) * H;
+    if (residual_out != residual && overlap(residual_out, th * 4, residual, th * 4))
+        return MF_ERR_ALIAS;
+    const void* ins[] = {partials, gamma};
+    const size_t in_bytes[] = {size_t(num_ranks) * th * 4, size_t(H) * 2};
+    for (int i = 0; i < 2; ++i) {
+        if (overlap(residual_out, th * 4, ins[i], in_bytes[i]) ||
+            overlap(out, th * 2, ins[i], in_bytes[i]))
+            return MF_ERR_ALIAS;
+    }
+    if (overlap(out, th * 2, residual, th * 4) || overlap(out, th * 2, residual_out, th * 4))
+        return MF_ERR_ALIAS;
+
+    CombineArgs a;
+    a.partials = partials;
+    a.residual = residual;
+    a.residual_out = residual_out;
+    a.gamma = gamma;
+    a.out = out;
+    a.T = T;
+    a.H = H;
+    a.G = num_ranks;
     a.eps = eps;
     void* args[] = {&a};
     return hip_status(hipLaunchKernel(fn, dim3((unsigned)s.grid), dim3(s.block), args, s.lds,

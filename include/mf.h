@@ -84,6 +84,38 @@ int mf_moe_finalize(const uint16_t* expert_rows, int64_t num_rows, const int32_t
                     int64_t T, int32_t H, int32_t k, void* stream);
 
 /*
+ * The expert-parallel split of the finalize ([PR6544] section 2.4: finalize + RMSNorm +
+ * all-reduce, where the slots of non-local experts skip normalisation; [PR4730] section 2: the
+ * all-reduce's sum fused with the residual add and RMSNorm).  Between the two calls the
+ * caller exchanges the partials (a reduce-scatter by token owner), which is not part of this
+ * library; on one GPU the partials of every rank can be computed and combined in place.
+ *
+ * mf_moe_finalize_ep_partial: this GPU's share.  For every token t:
+ *   partial[t,:] = +0; for j = 0..k-1 in order, skipping every slot with idx[t,j] < 0 (an
+ *   expert on another GPU: its row, expert id and weight are not read):
+ *       partial[t,:] = fma(weights[t,j], x_j, partial[t,:])      (x_j as in mf_moe_finalize)
+ *  Arguments as mf_moe_finalize's; partial fp32 [T, H] (16-byte aligned, overlapping no
+ *  input).  A token with no local slot gets +0.  num_rows >= 1 (pass any one-row buffer when
+ *  no expert is local).  idx >= num_rows is clamped (memory-safe, result unspecified).
+ *
+ * mf_moe_finalize_ep_combine: the token owner's step.  For every token t of its T tokens:
+ *   acc = +0; for g = 0..num_ranks-1 in order: acc = acc + partials[g, t, :]      (fp32)
+ *   residual_out[t,:] = residual[t,:] + acc
+ *   out[t,:] = bf16_rne(residual_out * (mean(residual_out^2) + eps)^-1/2 * gamma)
+ *  partials fp32 [num_ranks, T, H] (rank-major), 1 <= num_ranks <= 1024; the other arguments
+ *  and their checks as mf_moe_finalize's (residual_out may equal residual).
+ * With one rank holding every expert, partial + combine equal mf_moe_finalize bit for bit.
+ */
+int mf_moe_finalize_ep_partial(const uint16_t* expert_rows, int64_t num_rows,
+                               const int32_t* idx, const float* weights,
+                               const int32_t* expert_ids, const uint16_t* expert_gamma,
+                               int32_t num_experts, float eps, float* partial, int64_t T,
+                               int32_t H, int32_t k, void* stream);
+int mf_moe_finalize_ep_combine(const float* partials, int32_t num_ranks, const float* residual,
+                               float* residual_out, const uint16_t* gamma, float eps,
+                               uint16_t* out, int64_t T, int32_t H, void* stream);
+
+/*
  * Gated-residual RMSNorm ([PR6544] section 1.1; fixed hidden size 8192 there, any
  * supported H here):
  *   residual_out = residual + sigmoid(gate) * x                 (fp32, sigmoid = 1/(1+e^-g))

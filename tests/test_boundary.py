@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     L = ctypes.CDLL(mf.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -86,6 +86,41 @@ def fin(rows=A, num_rows=32, idx=B, w=C, eids=None, eg=None, E=0, res=D, res_out
 ])
 def test_finalize_rejects_bad_arguments(kw, code):
     assert fin(**kw) == code
+
+
+def ep_part(rows=A, num_rows=32, idx=B, w=C, eids=None, eg=None, E=0, eps=1e-6, part=D, T=16,
+            H=1024, k=2):
+    return mf.lib().mf_moe_finalize_ep_partial(rows, num_rows, idx, w, eids, eg, E, eps, part, T,
+                                               H, k, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), SHAPE), (dict(num_rows=-1), SHAPE), (dict(H=1030), UNSUP), (dict(k=65), UNSUP),
+    (dict(rows=None), NULL), (dict(idx=None), NULL), (dict(w=None), NULL), (dict(part=None), NULL),
+    (dict(eids=B + 4096), NULL), (dict(num_rows=0), SHAPE), (dict(eps=-1.0), VALUE),
+    (dict(part=D + 4), ALIGN), (dict(rows=A + 2), ALIGN), (dict(part=A + 64), ALIAS),
+    (dict(part=B), ALIAS), (dict(T=1 << 26), SHAPE),
+])
+def test_ep_partial_rejects_bad_arguments(kw, code):
+    assert ep_part(**kw) == code
+    assert ep_part(T=0) == OK
+
+
+def ep_comb(parts=A, G=8, res=B, res_out=C, gamma=D, eps=1e-6, out=E_, T=16, H=1024):
+    return mf.lib().mf_moe_finalize_ep_combine(parts, G, res, res_out, gamma, eps, out, T, H, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), SHAPE), (dict(G=0), SHAPE), (dict(G=1025), SHAPE), (dict(H=1020), UNSUP),
+    (dict(parts=None), NULL), (dict(res=None), NULL), (dict(res_out=None), NULL),
+    (dict(gamma=None), NULL), (dict(out=None), NULL), (dict(eps=float("nan")), VALUE),
+    (dict(parts=A + 8), ALIGN), (dict(out=E_ + 2), ALIGN), (dict(res_out=A + 16 * 1024 * 4 * 7), ALIAS),
+    (dict(out=A), ALIAS), (dict(res_out=B + 16), ALIAS), (dict(out=C + 64), ALIAS),
+])
+def test_ep_combine_rejects_bad_arguments(kw, code):
+    assert ep_comb(**kw) == code
+    assert ep_comb(T=0) == OK
+    assert ep_comb(T=0, res_out=B) == OK  # in place is allowed
 
 
 def test_finalize_zero_tokens_is_a_no_op():

@@ -24,7 +24,11 @@ Recipe (numpy ``default_rng(seed)``, PCG64; draws happen in the order listed):
        rounded to bfloat16 (round-to-nearest-even, by torch's CPU cast);
     5. residual ``[T, H]`` float32 ~ N(0, residual_std);
     6. gamma ``[H]`` = 1 + 0.1 * N(0, 1), rounded to bfloat16;
-    7. (per-expert variant only) expert gammas ``[E, H]`` = 1 + 0.1 * N(0, 1), bfloat16.
+    7. (per-expert variant only) expert gammas ``[E, H]`` = 1 + 0.1 * N(0, 1), bfloat16;
+    8. (expert-parallel view only, no draw) the slots of experts that live on other ranks
+       (expert e on rank e % ep_ranks) get idx -1.
+* Expert-parallel combine (``make_ep_combine_inputs``): partials ``[G, T, H]`` ~ N(0, std 0.5)
+  fp32, residual ``[T, H]`` ~ N(0, 1) fp32, gamma ``[H]`` = 1 + 0.1 * N(0, 1) bf16.
 * MoE routing (``make_route_inputs``): router logits ``[T, E]`` ~ N(0, 1) float32, optionally
   rounded to bfloat16 values (``bf16_logits``: the precision of a bf16 router GEMM, which
   makes exactly equal logits common).
@@ -58,6 +62,13 @@ WORKLOADS = {
     # Prefill-sized deterministic finalize: the throughput workload.
     "finalize_prefill": dict(kind="finalize", T=16384, H=7168, E=256, k=8, seed=3,
                              layout="expert_grouped", per_expert=False, residual_std=1.0),
+    # Expert parallelism over 8 GPUs at the prefill size: this GPU's partial (its 32 of the 256
+    # experts; the other slots are marked -1) and the owner's combine of 8 partials for its
+    # 2048 tokens.
+    "finalize_ep_partial": dict(kind="finalize", T=16384, H=7168, E=256, k=8, seed=9,
+                                layout="expert_grouped", per_expert=False, residual_std=1.0,
+                                ep_ranks=8, ep_rank=0),
+    "finalize_ep_combine": dict(kind="ep_combine", T=2048, H=7168, G=8, seed=10),
     # Gated-residual RMSNorm at its fixed hidden size.
     "gated_residual_rmsnorm": dict(kind="gated", T=4096, H=8192, seed=4),
     # The dual-output form: the same gated residual feeding this layer's and the next layer's
@@ -139,7 +150,8 @@ def unpermute_index(rng: np.random.Generator, expert_ids: np.ndarray, layout: st
 
 
 def make_finalize_inputs(T: int, H: int, E: int, k: int, seed: int, layout: str = "expert_grouped",
-                         per_expert: bool = False, residual_std: float = 1.0) -> dict:
+                         per_expert: bool = False, residual_std: float = 1.0, ep_ranks: int = 0,
+                         ep_rank: int = 0) -> dict:
     rng = np.random.default_rng(seed)
     expert_ids, w = draw_routing(rng, T, E, k)
     idx = unpermute_index(rng, expert_ids, layout)
@@ -151,7 +163,24 @@ def make_finalize_inputs(T: int, H: int, E: int, k: int, seed: int, layout: str 
              expert_gamma=None)
     if per_expert:
         d["expert_gamma"] = to_bf16_bits(1.0 + 0.1 * _normal_f32(rng, E * H)).reshape(E, H)
+    if ep_ranks:
+        # one GPU's view under expert parallelism: expert e lives on rank e % ep_ranks, and the
+        # slots of other ranks' experts are marked -1 (no draw: the same bytes otherwise)
+        d["kind"] = "ep_partial"
+        d["ep_ranks"], d["ep_rank"] = ep_ranks, ep_rank
+        d["idx"] = np.where(expert_ids % ep_ranks == ep_rank, idx, -1).astype(np.int32)
     return d
+
+
+def make_ep_combine_inputs(T: int, H: int, G: int, seed: int) -> dict:
+    """The token owner's inputs after the exchange: G partials [G, T, H] ~ N(0, 1/2) fp32 (a
+    weighted sum of a few unit rows per rank), residual ~ N(0, 1) fp32, gamma bf16."""
+    rng = np.random.default_rng(seed)
+    partials = _normal_f32(rng, G * T * H, 0.5).reshape(G, T, H)
+    residual = _normal_f32(rng, T * H).reshape(T, H)
+    gamma = to_bf16_bits(1.0 + 0.1 * _normal_f32(rng, H))
+    return dict(kind="ep_combine", T=T, H=H, G=G, eps=EPS, partials=partials, residual=residual,
+                gamma=gamma)
 
 
 def make_gated_inputs(T: int, H: int, seed: int, dual: bool = False) -> dict:
@@ -196,4 +225,6 @@ def make_inputs(name: str, **overrides) -> dict:
         return make_per_head_inputs(**cfg)
     if kind == "route":
         return make_route_inputs(**cfg)
+    if kind == "ep_combine":
+        return make_ep_combine_inputs(**cfg)
     raise ValueError(kind)
