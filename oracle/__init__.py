@@ -1,6 +1,7 @@
 """CPU oracle for the MoE finalize path (and its expert-parallel partial and combine steps), the
 sibling fused norms (gated residual RMSNorm, its dual-output "next" form, per-head RMSNorm with
-a sigmoid gate), and the routing and expert-sorted permutation the finalize consumes.
+a sigmoid gate), the MXFP4 quantisation of a normalised row, and the routing and expert-sorted
+permutation the finalize consumes.
 
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg
 of ``bench.py`` are the only callers.  The product path never imports this package, and
@@ -50,6 +51,8 @@ def _load():
         lib.oracle_gated_residual_next_rmsnorm.argtypes = [p, p, p, p, p, p, f32, p, p, i64, i32]
         lib.oracle_rmsnorm_sigmoid_gate.argtypes = [p, p, p, f32, p, i64, i32, i32]
         lib.oracle_moe_route.argtypes = [p, i64, i32, i32, p, p, p, p, p]
+        lib.oracle_mxfp4_quantize.argtypes = [p, i64, i32, p, p]
+        lib.oracle_rmsnorm_mxfp4_quantize.argtypes = [p, p, f32, p, p, i64, i32]
         lib.oracle_bf16_round.argtypes = [p, p, i64]
         lib.oracle_bf16_round.restype = None
         _lib = lib
@@ -210,6 +213,36 @@ def moe_route(logits, k):
     if st != 0:
         raise ValueError(f"oracle_moe_route failed with status {st}")
     return eids, w, idx, perm, off
+
+
+def mxfp4_quantize(x):
+    """MXFP4 of float32 values [T, H] (H % 32 == 0): (codes uint8 [T, H/2], two E2M1 codes per
+    byte, the even-indexed value in the low nibble; scale codes uint8 [T, H/32], E8M0)."""
+    lib = _load()
+    xa, px = _c(x, np.float32)
+    T, H = xa.shape
+    if H % 32:
+        raise ValueError("H must be a multiple of 32")
+    q = np.empty((T, H // 2), np.uint8)
+    sc = np.empty((T, H // 32), np.uint8)
+    lib.oracle_mxfp4_quantize(px, T, H, q.ctypes.data_as(ctypes.c_void_p),
+                              sc.ctypes.data_as(ctypes.c_void_p))
+    return q, sc
+
+
+def rmsnorm_mxfp4_quantize(x, gamma, eps):
+    """RMSNorm of bf16 rows x [T, H] with gamma, rounded to float32, then MXFP4 (as above)."""
+    lib = _load()
+    xa, px = _c(x, np.uint16)
+    g, pg = _c(gamma, np.uint16)
+    T, H = xa.shape
+    if H % 32:
+        raise ValueError("H must be a multiple of 32")
+    q = np.empty((T, H // 2), np.uint8)
+    sc = np.empty((T, H // 32), np.uint8)
+    lib.oracle_rmsnorm_mxfp4_quantize(px, pg, float(eps), q.ctypes.data_as(ctypes.c_void_p),
+                                      sc.ctypes.data_as(ctypes.c_void_p), T, H)
+    return q, sc
 
 
 def bf16_round(v):

@@ -1,8 +1,9 @@
 /*
  * Plain CPU oracle for the MoE finalize path (and its expert-parallel split into a partial
  * sum per GPU and a combine on the token's owner), its sibling fused norms (gated residual
- * RMSNorm, the dual-output gated residual norm, per-head RMSNorm with a sigmoid gate), and the
- * routing that produces the finalize's gather indices and weights.
+ * RMSNorm, the dual-output gated residual norm, per-head RMSNorm with a sigmoid gate), the
+ * MXFP4 block quantisation of a normalised row, and the routing that produces the finalize's
+ * gather indices and weights.
  *
  * Parity unpinned, as to meaning only: the dual-output gated residual norm is named by the
  * pages but not defined; the reading taken is stated at its function, whose arithmetic the
@@ -286,6 +287,90 @@ int oracle_gated_residual_next_rmsnorm(const uint16_t* x, const uint16_t* gate,
             on[h] = bf16_round((double)r[h] * s * bf16_value(gamma_next[h]));
         }
     }
+    return 0;
+}
+
+/*
+ * MXFP4 block quantisation: the PR #6544 page's RMSNorm + block-scaled FP4 quantisation
+ * (section 2.3; NVFP4 there), retargeted to the OCP Microscaling (MX) format, whose published
+ * definition is taken here because the pages do not define the format: blocks of 32
+ * consecutive values along a row share one E8M0 scale X = 2^e; each value is stored as
+ * E2M1 (sign, 2 exponent bits, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+ *     e = floor(log2(max_i |v_i|)) - 2         (2 = the largest E2M1 exponent), clamped to
+ *                                               [-127, 127]; an all-zero block takes e = -127
+ *     scale code = e + 127                      (one byte per block)
+ *     code_i = E2M1 nearest to v_i / 2^e, ties to the even code, |.| above 6 saturating to 6;
+ *              the sign bit follows v_i, also for zeros
+ * Two codes per byte, the even-indexed value in the low nibble.
+ */
+static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+static uint8_t e2m1_code(double v) {
+    const uint8_t sign = signbit(v) ? 8 : 0;
+    const double m = fabs(v);
+    if (m >= 6.0) return sign | 7;
+    uint8_t best = 0;
+    for (uint8_t c = 1; c < 8; ++c) {
+        const double d = fabs(m - kE2M1[c]), db = fabs(m - kE2M1[best]);
+        if (d < db || (d == db && (c & 1) == 0)) best = c; /* ties: the even code */
+    }
+    return sign | best;
+}
+
+static int mx_block_exponent(const double* v) {
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(v[i]));
+    if (amax == 0.0) return -127;
+    int e2;
+    frexp(amax, &e2); /* amax = m * 2^e2, m in [0.5, 1): floor(log2(amax)) = e2 - 1 */
+    int e = e2 - 1 - 2;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+static void mx_quantize_row(const double* v, int32_t H, uint8_t* q, uint8_t* scales) {
+    for (int32_t b = 0; b < H / 32; ++b) {
+        const double* blk = v + b * 32;
+        const int e = mx_block_exponent(blk);
+        scales[b] = (uint8_t)(e + 127);
+        for (int i = 0; i < 32; i += 2) {
+            const uint8_t lo = e2m1_code(ldexp(blk[i], -e)); /* exact: a power-of-two scale */
+            const uint8_t hi = e2m1_code(ldexp(blk[i + 1], -e));
+            q[(b * 32 + i) / 2] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}
+
+/* fp32 values [T, H] (H a multiple of 32) -> codes [T, H/2] and scale codes [T, H/32]. */
+int oracle_mxfp4_quantize(const float* x, int64_t T, int32_t H, uint8_t* q, uint8_t* scales) {
+    double* v = (double*)malloc(sizeof(double) * (size_t)(H > 0 ? H : 1));
+    if (!v) return -2;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < H; ++h) v[h] = (double)x[t * (int64_t)H + h];
+        mx_quantize_row(v, H, q + t * (int64_t)(H / 2), scales + t * (int64_t)(H / 32));
+    }
+    free(v);
+    return 0;
+}
+
+/*
+ * RMSNorm, then MXFP4 (the same page's section 2.3 without the all-gather):
+ *     y = fp32(x * rms_scale(x) * gamma)   (float64, rounded once to float32: the quantisation
+ *                                           decision is taken on float32 values, the
+ *                                           precision the kernel works in)
+ *     (q, scales) = mxfp4(y)
+ */
+int oracle_rmsnorm_mxfp4_quantize(const uint16_t* x, const uint16_t* gamma, float eps,
+                                  uint8_t* q, uint8_t* scales, int64_t T, int32_t H) {
+    double* v = (double*)malloc(sizeof(double) * (size_t)(H > 0 ? H : 1));
+    if (!v) return -2;
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t* xt = x + t * (int64_t)H;
+        double s = rms_scale_bf16(xt, H, eps);
+        for (int32_t h = 0; h < H; ++h)
+            v[h] = (double)(float)(bf16_value(xt[h]) * s * bf16_value(gamma[h]));
+        mx_quantize_row(v, H, q + t * (int64_t)(H / 2), scales + t * (int64_t)(H / 32));
+    }
+    free(v);
     return 0;
 }
 

@@ -391,6 +391,103 @@ def test_ep_remote_slots_skip_the_per_expert_norm():
     assert np.array_equal(p1, p2)
 
 
+# ----------------------------------------------------------------------------- MXFP4
+
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _mx_decode(q, sc):
+    """Values of MXFP4 codes (float64 [T, H])."""
+    lo, hi = q & 0xF, q >> 4
+    codes = np.stack([lo, hi], axis=-1).reshape(q.shape[0], -1)
+    mag = E2M1[codes & 7]
+    val = np.where(codes & 8, -mag, mag)
+    return val * np.repeat(np.ldexp(1.0, sc.astype(np.int64) - 127), 32, axis=1)
+
+
+def test_golden_mxfp4_hand_example():
+    g = json.load(open(GOLDEN))["mxfp4_quantize"]
+    head = [-0.0 if v == "-0" else float(v) for v in g["values_block0_head"]]
+    b0 = np.array(head + [0.0] * 16, np.float32)
+    x = np.concatenate([b0, b0 * np.float32(2.0 ** -10), np.zeros(32, np.float32)])[None]
+    q, sc = oracle.mxfp4_quantize(x)
+    want = [int(h, 16) for h in g["expected_block_bytes"]]
+    assert q[0, :16].tolist() == want and q[0, 16:32].tolist() == want
+    assert q[0, 32:].tolist() == [0] * 16
+    assert sc[0].tolist() == g["expected_scales"]
+
+
+def test_golden_rmsnorm_mxfp4_hand_example():
+    g = json.load(open(GOLDEN))["rmsnorm_mxfp4_quantize"]
+    H = g["H"]
+    x = workloads.to_bf16_bits(np.tile([1.0, -1.0], H // 2).astype(np.float32))[None]
+    for gam, key in ((1.0, "expected_scale_gamma1"), (0.5, "expected_scale_gamma_half")):
+        q, sc = oracle.rmsnorm_mxfp4_quantize(x, workloads.to_bf16_bits(np.full(H, gam, np.float32)),
+                                              g["eps"])
+        assert q[0].tolist() == [int(g["expected_byte"], 16)] * (H // 2)
+        assert sc[0].tolist() == [g[key]]
+
+
+def _nearest_ok(v, dec, sc):
+    """Every decoded value is the nearest E2M1 point of v / X (|v / X| above 6 saturates),
+    ties to the even code, and X = 2^(floor(log2(max|v|)) - 2) per block."""
+    T, H = v.shape
+    blocks = np.abs(v.astype(np.float64)).reshape(T, H // 32, 32).max(axis=-1)
+    m, e = np.frexp(blocks)
+    want = np.where(blocks == 0, 0, np.clip(e - 1 - 2 + 127, 0, 254))
+    assert np.array_equal(sc, want.astype(np.uint8))
+    X = np.repeat(np.ldexp(1.0, sc.astype(np.int64) - 127), 32, axis=1)
+    r = np.abs(v.astype(np.float64)) / X
+    d = np.abs(r[..., None] - E2M1)                     # distance to each grid point
+    best = d.min(axis=-1, keepdims=True)
+    cand = (d == best)
+    even = cand & (np.arange(8) % 2 == 0)
+    pick = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    pick = np.where(r >= 6, 7, pick)
+    assert np.array_equal(np.abs(dec) / X, E2M1[pick])
+    assert np.array_equal(np.signbit(dec), np.signbit(v))
+
+
+@pytest.mark.parametrize("T,H,spread", [(3, 64, 1.0), (5, 256, 30.0), (2, 4096, 1e-20), (4, 96, 1e20)])
+def test_mxfp4_is_the_nearest_grid_point(T, H, spread):
+    rng = np.random.default_rng(50 + H)
+    x = (rng.standard_normal((T, H)) * spread).astype(np.float32)
+    x[:, 5] = -0.0
+    x[0, 32:64] = 0.0                                   # an all-zero block
+    q, sc = oracle.mxfp4_quantize(x)
+    _nearest_ok(x, _mx_decode(q, sc), sc)
+
+
+def test_mxfp4_scale_equivariance_and_sign_symmetry():
+    rng = np.random.default_rng(51)
+    x = rng.standard_normal((4, 128)).astype(np.float32)
+    q, sc = oracle.mxfp4_quantize(x)
+    q2, sc2 = oracle.mxfp4_quantize(x * np.float32(2.0 ** 7))
+    assert np.array_equal(q, q2) and np.array_equal(sc2.astype(int), sc.astype(int) + 7)
+    qn, scn = oracle.mxfp4_quantize(-x)
+    assert np.array_equal(qn, q ^ 0x88) and np.array_equal(scn, sc)
+
+
+def test_rmsnorm_mxfp4_scale_invariance_and_brute_force():
+    d = workloads.make_gated_inputs(6, 512, seed=52)
+    x, gamma = d["x"], d["gamma"]
+    q, sc = oracle.rmsnorm_mxfp4_quantize(x, gamma, 0.0)
+    # RMSNorm with eps = 0 is invariant under x -> 2^m x, so the codes are unchanged
+    q2, sc2 = oracle.rmsnorm_mxfp4_quantize(workloads.to_bf16_bits(f32(x) * np.float32(8.0)), gamma,
+                                            0.0)
+    assert np.array_equal(q, q2) and np.array_equal(sc, sc2)
+    # against torch's float64 rms_norm: the decoded value is within half a grid step (or the
+    # saturation) of the normalised value
+    xt = torch.from_numpy(f32(x).astype(np.float64))
+    y = torch.nn.functional.rms_norm(xt, (512,), weight=torch.from_numpy(
+        f32(gamma).astype(np.float64)), eps=1e-6).numpy()
+    q, sc = oracle.rmsnorm_mxfp4_quantize(x, gamma, 1e-6)
+    dec = _mx_decode(q, sc)
+    X = np.repeat(np.ldexp(1.0, sc.astype(np.int64) - 127), 32, axis=1)
+    step = np.where(np.abs(y) / X < 2, 0.5, np.where(np.abs(y) / X < 4, 1.0, 2.0)) * X
+    assert np.all((np.abs(dec - y) <= 0.5 * step * 1.0001) | (np.abs(y) / X > 6))
+
+
 # ----------------------------------------------------------------------------- gated
 
 
