@@ -14,7 +14,8 @@ traffic: HBM bytes per launch measured with rocprofv3 counters, read from the co
 summary under profiles/ when it was taken from the current kernel sources, else null.
 cpu_baseline: the CPU oracle timed on a bounded sample of the same workload on the host.
 Other workloads (--workload) time the sibling kernels (the gated norms, single and dual output,
-and the per-head norm), the expert-parallel partial and combine steps, the routing producer (one step = one
+and the per-head norm), RMSNorm + MXFP4 quantisation, the expert-parallel partial and combine
+steps, the routing producer (one step = one
 mf_moe_route call: its three kernels, timed together by the events around the call) and the
 copy used for calibration.
 """
@@ -55,6 +56,8 @@ KERNEL_SOURCES = {
     "per_head": _NORM_SOURCES,
     "copy": _NORM_SOURCES,
     "route": ["mf_device.h", "route_kernels.h", "api_util.h", "route_api.hip"],
+    "rmsnorm_mx": ["mf_device.h", "row_norm.h", "mx_kernels.h", "api_util.h", "row_shape.h",
+                   "mx_api.hip"],
 }
 
 
@@ -97,6 +100,9 @@ def algorithmic_bytes(d: dict) -> int:
         if d.get("expert_gamma") is not None:
             b += T * k * 4 + len(np.unique(d["expert_ids"])) * H * 2
         return b
+    if kind == "rmsnorm_mx":
+        T, H = d["T"], d["H"]
+        return T * H * 2 + H * 2 + T * H // 2 + T * H // 32   # x, gamma in; codes, scales out
     if kind == "ep_partial":
         # local rows read, every idx read, local weights read, the fp32 partial written
         T, H, k = d["T"], d["H"], d["k"]
@@ -157,6 +163,11 @@ def upload(d: dict, dev):
                     gamma=up(d["gamma"], True),
                     res_out=torch.empty((T, H), dtype=torch.float32, device=dev),
                     out=torch.empty((T, H), dtype=torch.bfloat16, device=dev))
+    if kind == "rmsnorm_mx":
+        T, H = d["T"], d["H"]
+        return dict(x=up(d["x"], True), gamma=up(d["gamma"], True),
+                    q=torch.empty((T, H // 2), dtype=torch.uint8, device=dev),
+                    sc=torch.empty((T, H // 32), dtype=torch.uint8, device=dev))
     if kind == "ep_partial":
         T, H = d["T"], d["H"]
         return dict(rows=up(d["expert_rows"], True), idx=up(d["idx"]), w=up(d["weights"]),
@@ -204,6 +215,9 @@ def launcher(d: dict, g: dict):
         return lambda: mf.mf_gated_residual_rmsnorm(g["x"], g["gate"], g["res"], g["gamma"],
                                                     d["eps"], residual_out=g["res_out"],
                                                     out=g["out"])
+    if kind == "rmsnorm_mx":
+        return lambda: mf.mf_rmsnorm_mxfp4_quantize(g["x"], g["gamma"], d["eps"], q=g["q"],
+                                                    scales=g["sc"])
     if kind == "ep_partial":
         return lambda: mf.mf_moe_finalize_ep_partial(g["rows"], g["idx"], g["w"], d["eps"],
                                                      partial=g["part"])
@@ -233,7 +247,7 @@ def launch_config(name: str, d: dict) -> dict:
         pe = d.get("expert_gamma") is not None
         return mf.mf_launch_shape(mf.KIND_FINALIZE_PER_EXPERT if pe else mf.KIND_FINALIZE,
                                   d["T"], d["H"], d["k"])
-    if kind == "ep_combine":
+    if kind in ("ep_combine", "rmsnorm_mx"):
         return mf.mf_launch_shape(mf.KIND_GATED, d["T"], d["H"])  # the same row shape
     if kind in ("gated", "gated_next"):
         return mf.mf_launch_shape(mf.KIND_GATED, d["T"], d["H"])
@@ -270,6 +284,8 @@ def cpu_baseline(d: dict, target_cpu_s: float = 15.0, max_threads: int = 16) -> 
             oracle.rmsnorm_sigmoid_gate(d["x"][lo:hi], d["gate"][lo:hi], d["gamma"], d["eps"])
         elif kind == "route":
             oracle.moe_route(d["logits"][lo:hi], d["k"])
+        elif kind == "rmsnorm_mx":
+            oracle.rmsnorm_mxfp4_quantize(d["x"][lo:hi], d["gamma"], d["eps"])
         elif kind == "ep_partial":
             oracle.moe_finalize_ep_partial(d["expert_rows"], d["idx"][lo:hi], d["weights"][lo:hi],
                                            d["eps"])
@@ -320,7 +336,7 @@ def main() -> int:
                     choices=["finalize_prefill", "finalize_decode_per_expert", "finalize_tiny",
                              "gated_residual_rmsnorm", "gated_residual_next_rmsnorm",
                              "rmsnorm_sigmoid_gate", "moe_route_prefill", "finalize_ep_partial",
-                             "finalize_ep_combine",
+                             "finalize_ep_combine", "rmsnorm_mxfp4",
                              "moe_route_decode", "stream_copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

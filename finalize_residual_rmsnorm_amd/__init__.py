@@ -22,7 +22,8 @@ __all__ = [
     "mf_rmsnorm_sigmoid_gate_supported", "mf_launch_shape", "mf_stream_copy", "mf_status_string",
     "mf_moe_route", "mf_moe_route_supported", "mf_moe_route_workspace_bytes",
     "mf_gated_residual_next_rmsnorm", "mf_gated_residual_next_rmsnorm_supported",
-    "mf_moe_finalize_ep_partial", "mf_moe_finalize_ep_combine", "LIB_PATH",
+    "mf_moe_finalize_ep_partial", "mf_moe_finalize_ep_combine", "mf_mxfp4_quantize",
+    "mf_rmsnorm_mxfp4_quantize", "mf_mxfp4_supported", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmf.so")
@@ -64,6 +65,9 @@ def lib() -> ctypes.CDLL:
             "mf_gated_residual_next_rmsnorm_supported": [i32],
             "mf_moe_finalize_ep_partial": [p, i64, p, p, p, p, i32, f32, p, i64, i32, i32, p],
             "mf_moe_finalize_ep_combine": [p, i32, p, p, p, f32, p, i64, i32, p],
+            "mf_mxfp4_quantize": [p, i64, i32, p, p, p],
+            "mf_rmsnorm_mxfp4_quantize": [p, p, f32, p, p, i64, i32, p],
+            "mf_mxfp4_supported": [i32],
             "mf_moe_route_supported": [i32, i32],
             "mf_moe_route_workspace_bytes": [i64, i32, i32],
         }
@@ -341,3 +345,44 @@ def mf_moe_route(logits: torch.Tensor, k: int, *, expert_ids: torch.Tensor | Non
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream, dev))
     _check("mf_moe_route", st)
     return expert_ids, weights, idx, perm, offsets
+
+
+def mf_mxfp4_supported(H: int) -> bool:
+    return bool(lib().mf_mxfp4_supported(H))
+
+
+def _mx_outputs(T, H, dev, q, scales):
+    if q is None:
+        q = torch.empty((T, H // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+    return q, scales
+
+
+def mf_mxfp4_quantize(x: torch.Tensor, *, q: torch.Tensor | None = None,
+                      scales: torch.Tensor | None = None, stream=None):
+    """MXFP4 of fp32 rows x [T, H] (H % 32 == 0).  Returns (q uint8 [T, H/2]: two E2M1 codes per
+    byte, even value in the low nibble; scales uint8 [T, H/32]: E8M0 codes)."""
+    T, H = x.shape
+    q, scales = _mx_outputs(T, H, x.device, q, scales)
+    st = lib().mf_mxfp4_quantize(_dev(x, torch.float32, "x"), T, H,
+                                 _dev(q, torch.uint8, "q", (T, H // 2)),
+                                 _dev(scales, torch.uint8, "scales", (T, H // 32)),
+                                 _stream(stream, x.device))
+    _check("mf_mxfp4_quantize", st)
+    return q, scales
+
+
+def mf_rmsnorm_mxfp4_quantize(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, *,
+                              q: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                              stream=None):
+    """RMSNorm of bf16 rows x [T, H] with gamma, then MXFP4.  Returns (q, scales) as above."""
+    T, H = x.shape
+    q, scales = _mx_outputs(T, H, x.device, q, scales)
+    st = lib().mf_rmsnorm_mxfp4_quantize(_dev(x, torch.bfloat16, "x"),
+                                         _dev(gamma, torch.bfloat16, "gamma", (H,)), float(eps),
+                                         _dev(q, torch.uint8, "q", (T, H // 2)),
+                                         _dev(scales, torch.uint8, "scales", (T, H // 32)), T, H,
+                                         _stream(stream, x.device))
+    _check("mf_rmsnorm_mxfp4_quantize", st)
+    return q, scales

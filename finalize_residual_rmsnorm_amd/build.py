@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmf.so")
-SOURCES = [os.path.join(CSRC, name) for name in ("mf_api.hip", "norm_api.hip", "route_api.hip")]
+SOURCES = [os.path.join(CSRC, name)
+           for name in ("mf_api.hip", "norm_api.hip", "route_api.hip", "mx_api.hip")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -1,0 +1,142 @@
+// MXFP4 block quantisation on gfx950, alone and after an RMSNorm.
+//
+// What it computes (page "FlashInfer: fused norms and TP/EP MoE for Muse-Spark-Open", PR #6544,
+// section 2.3: RMSNorm + block-scaled FP4 quantisation, NVFP4 there; retargeted to the OCP
+// Microscaling MXFP4 format, from its published definition): blocks of 32 consecutive values of
+// a row share one E8M0 scale X = 2^e, e = floor(log2(max|v|)) - 2 clamped to [-127, 127] (an
+// all-zero block takes -127); each value is stored as the E2M1 code nearest to v / X (ties to
+// the even code, saturating at 6, the sign kept for zeros), two codes per byte with the
+// even-indexed value in the low nibble.
+//
+// How it maps onto CDNA4:
+//  - A lane holds 8 consecutive values, so a block of 32 is one quad of lanes; the block maximum
+//    is a DPP max over the quad.
+//  - e + 127 is the biased exponent of the block maximum minus 2 (floor(log2) of a float is its
+//    exponent field), clamped at 0.
+//  - The conversion is gfx950's v_cvt_scalef32_pk_fp4_f32: two fp32 values divided by the
+//    power-of-two scale, rounded to nearest even and saturated, into one byte; four of them
+//    fill the lane's 32-bit word of codes.
+#pragma once
+
+#include "row_norm.h"
+
+namespace mf {
+
+// The E8M0 scale code of a block from its maximum magnitude (>= 0), and the scale as an fp32
+// power of two (2^-127, code 0, is a denormal: the conversion takes it as 2^-127).
+__device__ __forceinline__ uint32_t mx_scale_code(float amax) {
+    const int be = int((__float_as_uint(amax) >> 23) & 0xFFu);
+    return uint32_t(be > 2 ? be - 2 : 0);
+}
+
+__device__ __forceinline__ float mx_scale_value(uint32_t code) {
+    return __uint_as_float(code > 0 ? code << 23 : 0x00400000u);
+}
+
+// Maximum of |v| over the lane's 8 values and its quad (lanes 4q .. 4q+3, all active).
+__device__ __forceinline__ float mx_block_max(const float (&v)[8]) {
+    float m = __builtin_fabsf(v[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+    m = __builtin_fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+    m = __builtin_fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+    return m;
+}
+
+// The lane's 8 codes, value 2i in the low nibble of byte i.
+__device__ __forceinline__ uint32_t mx_pack8(const float (&v)[8], float scale) {
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], scale, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], scale, 3);
+    return w;
+}
+
+// ---------------------------------------------------------------------------------------
+// fp32 [T, H] -> codes [T, H/2], scales [T, H/32] (H % 32 == 0).  Flat over 8-value chunks:
+// chunk c covers values [8c, 8c + 8) of the flattened array; a block never crosses a row
+// because H / 8 is a multiple of 4.  Chunks past the end (whole quads, since the chunk count
+// is a multiple of 4) load a clamped chunk and store nothing.
+struct MxArgs {
+    const float* x;
+    uint8_t* q;
+    uint8_t* scales;
+    int64_t chunks;  // T * H / 8
+};
+
+constexpr int kMxThreads = 256;
+
+__global__ void __launch_bounds__(kMxThreads) mxfp4_quantize_kernel(const MxArgs a) {
+    const int64_t c = int64_t(blockIdx.x) * kMxThreads + threadIdx.x;
+    const int64_t cl = c < a.chunks ? c : a.chunks - 1;
+    const f32x4 lo = ld_stream(reinterpret_cast<const f32x4*>(a.x + cl * 8));
+    const f32x4 hi = ld_stream(reinterpret_cast<const f32x4*>(a.x + cl * 8 + 4));
+    const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const uint32_t code = mx_scale_code(mx_block_max(v));
+    const uint32_t w = mx_pack8(v, mx_scale_value(code));
+    if (c < a.chunks) {
+        reinterpret_cast<uint32_t*>(a.q)[c] = w;
+        if ((threadIdx.x & 3) == 0) a.scales[c / 4] = uint8_t(code);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// RMSNorm of bf16 rows, then MXFP4: the row framework of the fused norms (one workgroup per
+// token), y = (x * inv) * gamma in fp32 exactly as the bf16 RMSNorm output is formed, then the
+// quantisation above per slot.  H % 32 == 0, so a quad is wholly inside or wholly past the row.
+struct RmsMxArgs {
+    const uint16_t* x;      // bf16 [T, H]
+    const uint16_t* gamma;  // bf16 [H]
+    uint8_t* q;             // [T, H/2]
+    uint8_t* scales;        // [T, H/32]
+    int64_t T;
+    int32_t H;
+    float eps;
+};
+
+template <int VPL, int TAIL>
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(VPL == 1 ? 8 : 4, 8)))
+rmsnorm_mxfp4_kernel(const RmsMxArgs a) {
+    extern __shared__ float lds[];
+    const RowMap m = row_map();
+    const int H = a.H;
+    const Slots<VPL, TAIL> sl = slot_offsets<VPL, TAIL>(m, H);
+    const uint16_t* xr = a.x + m.t * H;
+
+    u32x4 xv[VPL], gm[VPL];
+#pragma unroll
+    for (int s = 0; s < VPL; ++s)
+        xv[s] = sl.suni[s] ? ld_stream(at<u32x4>(xr, sl.eoff[s] * 2u)) : u32x4{0u, 0u, 0u, 0u};
+    load_gamma(gm, a.gamma, sl);
+    float x[VPL][8];
+#pragma unroll
+    for (int s = 0; s < VPL; ++s) {
+        widen8(xv[s], x[s]);
+        if (!sl.sval[s]) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[s][i] = 0.0f;
+        }
+    }
+    float ss[1] = {lane_sumsq(x, sl)};
+    TokenLds L = token_lds(lds, m.wpt, 1);
+    token_sum<1>(ss, L, m);
+    const float inv = 1.0f / __builtin_sqrtf(ss[0] / (float)H + a.eps);
+    uint8_t* qr = a.q + m.t * (H / 2);
+    uint8_t* sr = a.scales + m.t * (H / 32);
+#pragma unroll
+    for (int s = 0; s < VPL; ++s) {
+        float g[8], y[8];
+        widen8(gm[s], g);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = (x[s][i] * inv) * g[i];
+        const uint32_t code = mx_scale_code(mx_block_max(y));
+        const uint32_t w = mx_pack8(y, mx_scale_value(code));
+        if (sl.sval[s]) {
+            *at<uint32_t>(qr, sl.eoff[s] / 2u) = w;
+            if ((m.lane & 3) == 0) sr[sl.eoff[s] / 32u] = uint8_t(code);
+        }
+    }
+}
+
+}  // namespace mf

@@ -12,6 +12,8 @@
  *           (fusion strategy: expert sum, residual add and RMSNorm in one launch).
  *  [PR4130] "FlashInfer: fused kernels and an optimised scheduler for MoE", code analysis
  *           items 1-3 (grouped GEMM over m_indptr rows; the warp-cooperative scheduler).
+ *  OCP Microscaling Formats (MX) specification: the MXFP4 format (E8M0 block scales over
+ *           32 values, E2M1 elements) used for the FP4 quantisation.
  *
  * Conventions for every entry point:
  *  - Tensors are dense and row-major.  bfloat16 data is passed as raw 16-bit patterns
@@ -156,6 +158,29 @@ int mf_rmsnorm_sigmoid_gate(const uint16_t* x, const uint16_t* gate, const uint1
                             int32_t head_dim, void* stream);
 
 /*
+ * MXFP4 block quantisation ([PR6544] section 2.3: RMSNorm + block-scaled FP4 quantisation,
+ * NVFP4 there; here the OCP Microscaling MXFP4 format, from its published definition).  Along
+ * each row, blocks of 32 consecutive values share one E8M0 scale X = 2^e,
+ *   e = floor(log2(max |v|)) - 2, clamped to [-127, 127] (an all-zero block takes -127),
+ *   scales[t, b] = e + 127
+ * and every value is stored as the E2M1 code (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; bit 3 the
+ * sign, kept for zeros) nearest to v / X, ties to the even code, magnitudes above 6 saturating
+ * to 6.  q[t, i] holds the codes of values 2i (low nibble) and 2i+1 (high nibble).
+ *
+ * mf_mxfp4_quantize: x fp32 [T, H] (16-byte aligned) -> q uint8 [T, H/2] (4-byte aligned),
+ *   scales uint8 [T, H/32].
+ * mf_rmsnorm_mxfp4_quantize: x bf16 [T, H], gamma bf16 [H] (16-byte aligned), eps >= 0:
+ *   y = fp32((x * (mean(x^2) + eps)^-1/2) * gamma) (as the bf16 RMSNorm outputs above, before
+ *   their rounding), then q, scales = MXFP4(y).
+ * Supported: H % 32 == 0 and 32 <= H <= 32768.  No output may overlap an input or the other
+ * output.  Inputs must be finite (other values give unspecified codes).
+ */
+int mf_mxfp4_quantize(const float* x, int64_t T, int32_t H, uint8_t* q, uint8_t* scales,
+                      void* stream);
+int mf_rmsnorm_mxfp4_quantize(const uint16_t* x, const uint16_t* gamma, float eps, uint8_t* q,
+                              uint8_t* scales, int64_t T, int32_t H, void* stream);
+
+/*
  * MoE routing and the expert-sorted permutation: the producer of the finalize's idx and
  * weights, and of the per-expert row ranges of the grouped GEMM that writes expert_rows
  * ([PR4130] code analysis items 1-3: the m_indptr / token_offset layout of the grouped GEMM
@@ -206,6 +231,7 @@ int mf_gated_residual_rmsnorm_supported(int32_t H);
 int mf_gated_residual_next_rmsnorm_supported(int32_t H);
 int mf_rmsnorm_sigmoid_gate_supported(int32_t head_dim);
 int mf_moe_route_supported(int32_t num_experts, int32_t k);
+int mf_mxfp4_supported(int32_t H);
 
 /*
  * Launch shape that mf_moe_finalize / mf_gated_residual_rmsnorm use for a problem size:

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 19, names
     L = ctypes.CDLL(mf.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -121,6 +121,31 @@ def test_ep_combine_rejects_bad_arguments(kw, code):
     assert ep_comb(**kw) == code
     assert ep_comb(T=0) == OK
     assert ep_comb(T=0, res_out=B) == OK  # in place is allowed
+
+
+def test_mxfp4_rejects_bad_arguments():
+    L = mf.lib()
+    q = L.mf_mxfp4_quantize
+    assert q(A, -1, 64, B, C, None) == SHAPE
+    assert q(A, 4, 48, B, C, None) == UNSUP          # H % 32 != 0
+    assert q(A, 4, 32800, B, C, None) == UNSUP
+    assert q(A, 0, 64, B, C, None) == OK
+    assert q(None, 4, 64, B, C, None) == NULL
+    assert q(A, 4, 64, None, C, None) == NULL
+    assert q(A + 8, 4, 64, B, C, None) == ALIGN
+    assert q(A, 4, 64, B + 2, C, None) == ALIGN
+    assert q(A, 4, 64, A + 64, C, None) == ALIAS
+    assert q(A, 4, 64, B, B + 64, None) == ALIAS     # q is 128 bytes
+    r = L.mf_rmsnorm_mxfp4_quantize
+    assert r(A, D, 1e-6, B, C, -1, 64, None) == SHAPE
+    assert r(A, D, 1e-6, B, C, 4, 40, None) == UNSUP
+    assert r(A, None, 1e-6, B, C, 4, 64, None) == NULL
+    assert r(A, D, -1.0, B, C, 4, 64, None) == VALUE
+    assert r(A, D + 4, 1e-6, B, C, 4, 64, None) == ALIGN
+    assert r(A, D, 1e-6, D, C, 4, 64, None) == ALIAS
+    assert r(A, D, 1e-6, B, A + 100, 4, 64, None) == ALIAS
+    assert r(A, D, 1e-6, B, C, 0, 64, None) == OK
+    assert mf.mf_mxfp4_supported(7168) and not mf.mf_mxfp4_supported(7176)
 
 
 def test_finalize_zero_tokens_is_a_no_op():

@@ -1,0 +1,167 @@
+"""Parity of the MXFP4 kernels on the GPU (through the C ABI) with the oracle.
+
+Bars:
+  - mf_mxfp4_quantize (fp32 in): codes and scales bit-identical (the OCP definition has one
+    answer for an fp32 value: the scale from the block maximum's exponent, the nearest code
+    with ties to even);
+  - mf_rmsnorm_mxfp4_quantize: the quantisation decision is taken on the fp32 normalised value,
+    which the GPU forms from its own fp32 mean square (a few ulps from the oracle's float64
+    one, rounded to fp32).  So every scale must be one the oracle's rule gives for a block
+    maximum within a relative band of 2^-20 of the oracle's, and every decoded value one its
+    rule gives for a value within that band of the oracle's; and >= 99.9% of all codes and
+    scales are bit-identical.
+Each case prints its name and sizes before it runs.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import finalize_residual_rmsnorm_amd as mf
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_examples.json")
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+BAND = 2.0 ** -20
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def quantize_gpu(x):
+    q, sc = mf.mf_mxfp4_quantize(torch.from_numpy(np.ascontiguousarray(x)).to(DEV))
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), sc.cpu().numpy()
+
+
+def decode(q, sc):
+    codes = np.stack([q & 0xF, q >> 4], axis=-1).reshape(q.shape[0], -1)
+    mag = E2M1[codes & 7]
+    val = np.where(codes & 8, -mag, mag)
+    return val * np.repeat(np.ldexp(1.0, sc.astype(np.int64) - 127), 32, axis=1)
+
+
+def test_mxfp4_golden_hand_example():
+    g = json.load(open(GOLDEN))["mxfp4_quantize"]
+    head = [-0.0 if v == "-0" else float(v) for v in g["values_block0_head"]]
+    b0 = np.array(head + [0.0] * 16, np.float32)
+    x = np.concatenate([b0, b0 * np.float32(2.0 ** -10), np.zeros(32, np.float32)])[None]
+    say("mxfp4 golden: T=1 H=96")
+    q, sc = quantize_gpu(x)
+    want = [int(h, 16) for h in g["expected_block_bytes"]]
+    assert q[0, :16].tolist() == want and q[0, 16:32].tolist() == want
+    assert q[0, 32:].tolist() == [0] * 16 and sc[0].tolist() == g["expected_scales"]
+
+
+@pytest.mark.parametrize("T,H,spread", [
+    (1, 32, 1.0), (3, 64, 1.0), (7, 96, 30.0), (5, 4096, 1e-20), (4, 8192, 1e20),
+    (1000, 7168, 1.0), (33, 32768, 0.01), (2, 1024, 1e-38),
+])
+def test_mxfp4_quantize_matches_oracle(T, H, spread):
+    say(f"mxfp4 quantize T={T} H={H} spread={spread}")
+    rng = np.random.default_rng(800 + T + H)
+    x = (rng.standard_normal((T, H)) * spread).astype(np.float32)
+    x[:, 3] = -0.0
+    if H >= 64:
+        x[0, 32:64] = 0.0                                           # an all-zero block
+    # exact ties and saturation inside one block of the first row
+    x[0, :16] = np.array([6, 3, 1.5, 0.5, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, 7, 0.3, 4, -2.5, -5],
+                         np.float32) * np.float32(spread)
+    q, sc = quantize_gpu(x)
+    q_ref, sc_ref = oracle.mxfp4_quantize(x)
+    assert np.array_equal(sc, sc_ref), f"{(sc != sc_ref).sum()} scales differ"
+    assert np.array_equal(q, q_ref), f"{(q != q_ref).sum()} code bytes differ"
+
+
+def test_mxfp4_quantize_every_code_and_tie():
+    # every E2M1 magnitude and every midpoint between neighbours, both signs, at three scales
+    mags = np.concatenate([E2M1, (E2M1[:-1] + E2M1[1:]) / 2, [6.5, 7.9]])
+    vals = np.concatenate([mags, -mags])
+    blocks = []
+    for e in (-100, 0, 100):
+        v = np.zeros(64)
+        v[:len(vals)] = vals
+        v[63] = 7.5                                                  # pins the block maximum
+        blocks.append(np.ldexp(v, e))
+    x = np.stack(blocks).astype(np.float32)
+    say(f"mxfp4 quantize: every code and tie, {x.shape}")
+    q, sc = quantize_gpu(x)
+    q_ref, sc_ref = oracle.mxfp4_quantize(x)
+    assert np.array_equal(sc, sc_ref) and np.array_equal(q, q_ref)
+
+
+def rms_mx_gpu(x, gamma, eps):
+    q, sc = mf.mf_rmsnorm_mxfp4_quantize(
+        torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(DEV),
+        torch.from_numpy(gamma.view(np.int16)).view(torch.bfloat16).to(DEV), eps)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), sc.cpu().numpy()
+
+
+def nearest(r):
+    """Signed E2M1 value nearest to r (ties to the even code, saturating at 6)."""
+    m = np.abs(r)
+    d = np.abs(m[..., None] - E2M1)
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    even = cand & (np.arange(8) % 2 == 0)
+    pick = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    pick = np.where(m >= 6, 7, pick)
+    return np.where(np.signbit(r), -E2M1[pick], E2M1[pick])
+
+
+def check_rms_mx(x, gamma, eps):
+    q, sc = rms_mx_gpu(x, gamma, eps)
+    q_ref, sc_ref = oracle.rmsnorm_mxfp4_quantize(x, gamma, eps)
+    T, H = x.shape
+    # the oracle's fp32 normalised value, and a band around it
+    xd = workloads.bf16_bits_to_f32(x).astype(np.float64)
+    s = 1.0 / np.sqrt((xd * xd).mean(axis=1, keepdims=True) + eps)
+    y = (xd * s * workloads.bf16_bits_to_f32(gamma)).astype(np.float32).astype(np.float64)
+    lo, hi = y * (1 - BAND), y * (1 + BAND)
+    # scales: a code the rule gives for a block maximum inside the band
+    amax = np.abs(y).reshape(T, H // 32, 32).max(axis=-1)
+    code = lambda a: np.where(a == 0, 0, np.clip(np.frexp(a)[1] - 1 - 2 + 127, 0, 254))
+    c_lo, c_hi = code(amax * (1 - BAND)), code(amax * (1 + BAND))
+    assert np.all((sc >= c_lo) & (sc <= c_hi)), f"{((sc < c_lo) | (sc > c_hi)).sum()} scales outside"
+    # values: with the GPU's scale, the code the rule gives for a value inside the band
+    X = np.repeat(np.ldexp(1.0, sc.astype(np.int64) - 127), 32, axis=1)
+    dec = decode(q, sc)
+    v1, v2 = nearest(lo / X) * X, nearest(hi / X) * X
+    ok = (dec >= np.minimum(v1, v2)) & (dec <= np.maximum(v1, v2))
+    assert ok.all(), f"{(~ok).sum()} codes outside the band"
+    exact = ((q == q_ref).sum() + (sc == sc_ref).sum()) / (q.size + sc.size)
+    assert exact >= 0.999, f"bit-identical fraction {exact:.5f}"
+    say(f"    bit-identical fraction {exact:.6f}")
+
+
+def test_rmsnorm_mxfp4_golden():
+    g = json.load(open(GOLDEN))["rmsnorm_mxfp4_quantize"]
+    H = g["H"]
+    x = workloads.to_bf16_bits(np.tile([1.0, -1.0], H // 2).astype(np.float32))[None]
+    say("rmsnorm mxfp4 golden: T=1 H=32")
+    for gam, key in ((1.0, "expected_scale_gamma1"), (0.5, "expected_scale_gamma_half")):
+        q, sc = rms_mx_gpu(x, workloads.to_bf16_bits(np.full(H, gam, np.float32)), g["eps"])
+        assert q[0].tolist() == [int(g["expected_byte"], 16)] * (H // 2)
+        assert sc[0].tolist() == [g[key]]
+
+
+@pytest.mark.parametrize("T,H", [(1, 32), (3, 544), (100, 7168), (7, 32768), (2049, 1024),
+                                 (5, 12288)])
+def test_rmsnorm_mxfp4_matches_oracle(T, H):
+    say(f"rmsnorm mxfp4 T={T} H={H}")
+    d = workloads.make_rmsnorm_mx_inputs(T, H, seed=900 + T + H)
+    check_rms_mx(d["x"], d["gamma"], d["eps"])
+
+
+def test_rmsnorm_mxfp4_workload_full_size():
+    d = workloads.make_inputs("rmsnorm_mxfp4")
+    say("rmsnorm mxfp4 workload T=4096 H=8192")
+    check_rms_mx(d["x"], d["gamma"], d["eps"])

@@ -36,6 +36,8 @@ Recipe (numpy ``default_rng(seed)``, PCG64; draws happen in the order listed):
   gate ``[T, H]`` ~ N(0, 2) bf16 (standard deviation 2), residual ``[T, H]`` ~ N(0, 1) fp32,
   gamma ``[H]`` = 1 + 0.1 * N(0, 1) bf16; with ``dual=True`` then gamma_next ``[H]``, drawn
   the same way.
+* RMSNorm + MXFP4 (``make_rmsnorm_mx_inputs``): x ``[T, H]`` ~ N(0, 1) bf16, gamma ``[H]`` =
+  1 + 0.1 * N(0, 1) bf16.
 * Per-head RMSNorm + sigmoid gate (``make_per_head_inputs``): x ``[T, heads, D]`` ~ N(0, 1)
   bf16, gate ``[T, heads, D]`` ~ N(0, 2) bf16, gamma ``[D]`` = 1 + 0.1 * N(0, 1) bf16.
 
@@ -74,6 +76,8 @@ WORKLOADS = {
     # The dual-output form: the same gated residual feeding this layer's and the next layer's
     # RMSNorm (two gammas), at the same fixed hidden size.
     "gated_residual_next_rmsnorm": dict(kind="gated", T=4096, H=8192, seed=8, dual=True),
+    # RMSNorm + MXFP4 quantisation of bf16 rows at hidden size 8192.
+    "rmsnorm_mxfp4": dict(kind="rmsnorm_mx", T=4096, H=8192, seed=11),
     # Per-head RMSNorm + sigmoid gate at its fixed head dim.
     "rmsnorm_sigmoid_gate": dict(kind="per_head", T=4096, heads=64, D=64, seed=5),
     # Routing that produces the prefill finalize's gather indices and weights.
@@ -196,6 +200,13 @@ def make_gated_inputs(T: int, H: int, seed: int, dual: bool = False) -> dict:
     return d
 
 
+def make_rmsnorm_mx_inputs(T: int, H: int, seed: int) -> dict:
+    rng = np.random.default_rng(seed)
+    x = _normal_bf16(rng, T * H).reshape(T, H)
+    gamma = to_bf16_bits(1.0 + 0.1 * _normal_f32(rng, H))
+    return dict(kind="rmsnorm_mx", T=T, H=H, eps=EPS, x=x, gamma=gamma)
+
+
 def make_per_head_inputs(T: int, heads: int, D: int, seed: int) -> dict:
     rng = np.random.default_rng(seed)
     x = _normal_bf16(rng, T * heads * D).reshape(T, heads, D)
@@ -227,4 +238,6 @@ def make_inputs(name: str, **overrides) -> dict:
         return make_route_inputs(**cfg)
     if kind == "ep_combine":
         return make_ep_combine_inputs(**cfg)
+    if kind == "rmsnorm_mx":
+        return make_rmsnorm_mx_inputs(**cfg)
     raise ValueError(kind)
