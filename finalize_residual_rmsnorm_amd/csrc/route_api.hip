@@ -46,13 +46,17 @@ int64_t route_workspace_bytes(const RoutePlan& p, int32_t E) {
     return (p.nblocks + 1) * int64_t(E) * int64_t(sizeof(int32_t));
 }
 
-const void* route_select_fn(int epl) {
+// The select kernel for a logits-per-lane count; vec: E a multiple of it and the logits
+// aligned to it (only the lane-major widths 2 and 4 have a vector form).
+const void* route_select_fn(int epl, bool vec) {
     switch (epl) {
-        case 1: return reinterpret_cast<const void*>(&route_select_kernel<1>);
-        case 2: return reinterpret_cast<const void*>(&route_select_kernel<2>);
-        case 4: return reinterpret_cast<const void*>(&route_select_kernel<4>);
-        case 8: return reinterpret_cast<const void*>(&route_select_kernel<8>);
-        case 16: return reinterpret_cast<const void*>(&route_select_kernel<16>);
+        case 1: return reinterpret_cast<const void*>(&route_select_kernel<1, false>);
+        case 2: return vec ? reinterpret_cast<const void*>(&route_select_kernel<2, true>)
+                           : reinterpret_cast<const void*>(&route_select_kernel<2, false>);
+        case 4: return vec ? reinterpret_cast<const void*>(&route_select_kernel<4, true>)
+                           : reinterpret_cast<const void*>(&route_select_kernel<4, false>);
+        case 8: return reinterpret_cast<const void*>(&route_select_kernel<8, false>);
+        case 16: return reinterpret_cast<const void*>(&route_select_kernel<16, false>);
         default: return nullptr;
     }
 }
@@ -112,7 +116,8 @@ int mf_moe_route(const float* logits, int64_t T, int32_t num_experts, int32_t k,
     void* args[] = {&a};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (p.nblocks > 0) {
-        const hipError_t e = hipLaunchKernel(route_select_fn(p.epl), dim3(unsigned(p.nblocks)),
+        const bool vec = (p.epl == 2 || p.epl == 4) && E % p.epl == 0 && aligned(logits, 4 * p.epl);
+        const hipError_t e = hipLaunchKernel(route_select_fn(p.epl, vec), dim3(unsigned(p.nblocks)),
                                              dim3(kRouteWaves * kWave), args,
                                              route_select_lds_bytes(E), s);
         if (e != hipSuccess) return MF_ERR_HIP;

@@ -17,10 +17,12 @@
 //
 // Three launches:
 //  1. route_select_kernel: one wave per run of `tpw` consecutive tokens, 16 waves per block.
-//     Top-k in k rounds: the wave-wide maximum of the order-preserving 32-bit image of the
-//     logits (DPP max within rows of 16 lanes, then across the four rows), then a ballot per
-//     logit register finds the lowest expert id holding that maximum (exact and tie-correct),
-//     whose logit is retired; the softmax; then each wave ranks its own slots (contiguous, in
+//     Top-k in k rounds over the order-preserving 32-bit image of the logits, each round a
+//     wave-wide maximum (DPP max within rows of 16 lanes, then across the four rows) and an
+//     exact tie-break to the lowest expert id: up to 4 logits per lane (E <= 256), every lane
+//     keeps its logits sorted and a round pops the head of the lowest lane holding the maximum;
+//     beyond that, a ballot per logit register finds the lowest id, whose logit is retired; the
+//     softmax; then each wave ranks its own slots (contiguous, in
 //     slot order) by expert in 64-slot chunks: a slot's rank among the earlier slots of its chunk with the same
 //     expert comes from ballots over the bits of the expert id (the ballot / prefix-count
 //     technique of the PR #4130 page's warp-cooperative scheduler, "why is this good" item 2),
@@ -99,31 +101,159 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
 // Maximum over the 64 lanes (every lane active), wave-uniform: within each row of 16 lanes
-// through DPP (quad swaps, half-row mirror, row mirror), then over the four rows.
+// through DPP (quad swaps, half-row mirror, row mirror), then across the rows with the row
+// broadcasts (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3), leaving the maximum in
+// lane 63.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_rows_u32(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, ROWS, 0xF, false));
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = umax(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
     v = umax(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
     v = umax(v, dpp_u32<0x141>(v));  // row_half_mirror
     v = umax(v, dpp_u32<0x140>(v));  // row_mirror
-    const uint32_t a = umax(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16));
-    const uint32_t b = umax(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48));
-    return umax(a, b);
+    v = umax(v, dpp_rows_u32<0x142, 0xA>(v));  // row_bcast:15 (disabled rows take 0: no change)
+    v = umax(v, dpp_rows_u32<0x143, 0xC>(v));  // row_bcast:31
+    return __builtin_amdgcn_readlane(v, kWave - 1);
 }
 
-// Logits of one token: lane l holds experts q*64 + l.  The loads are unconditional (lanes past
-// E read expert E-1 and their value is ignored): with no branch around them the compiler can
-// wait for exactly the loads a use needs, so the next token's loads stay in flight.
-template <int EPL>
+// Logits of one token.  LANE_MAJOR: lane l holds experts l*EPL + q; otherwise experts q*64 + l.
+// The loads are unconditional (experts past E read expert E-1 and their value is ignored): with
+// no branch around them the compiler can wait for exactly the loads a use needs, so the next
+// token's loads stay in flight.
+// VEC (lane-major, E a multiple of EPL, rows aligned to EPL floats): one EPL-wide load per lane,
+// lanes past E reading the last group.
+template <int EPL, bool LANE_MAJOR, bool VEC>
 __device__ __forceinline__ void load_logits(float (&x)[EPL], const float* row, int E, int lane) {
+    if constexpr (VEC && EPL == 4) {
+        const int g = lane * 4 < E ? lane : E / 4 - 1;
+        const f32x4 v = ld_stream(reinterpret_cast<const f32x4*>(row) + g);
 #pragma unroll
-    for (int q = 0; q < EPL; ++q) {
-        const int e = q * kWave + lane;
-        x[q] = ld_stream(row + (e < E ? e : E - 1));
+        for (int q = 0; q < 4; ++q) x[q] = v[q];
+    } else if constexpr (VEC && EPL == 2) {
+        const int g = lane * 2 < E ? lane : E / 2 - 1;
+        const f32x2 v = ld_stream(reinterpret_cast<const f32x2*>(row) + g);
+        x[0] = v[0];
+        x[1] = v[1];
+    } else {
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) {
+            const int e = LANE_MAJOR ? lane * EPL + q : q * kWave + lane;
+            x[q] = ld_stream(row + (e < E ? e : E - 1));
+        }
     }
 }
 
-// EPL: logits per lane, E <= 64 * EPL.
+// Largest number of logits per lane that the sorted selection handles (sorting more per lane
+// costs more than it saves).
+constexpr int kSortedMaxEpl = 4;
+
+// Top-k with experts laid out lane-major (lane l holds l*EPL .. l*EPL + EPL-1).  Each lane sorts
+// its logits once, largest first and equal logits by lower expert id; a round is then the wave
+// maximum of the lanes' heads, the lowest lane whose head holds it (a ballot: lanes hold
+// ascending id ranges, and a lane's head is its lowest id with that value), that head's id, and
+// a pop of that lane's list.  Exact and tie-correct, like the strided form below, with a fraction
+// of its scalar work per round.  Lane j < k receives selection j.
 template <int EPL>
+__device__ __forceinline__ void select_sorted(const float (&x)[EPL], int lane, int E, int k,
+                                              int& my_e, float& my_v, float& top) {
+    uint32_t s[EPL], my_o = 0, top_o = 0;
+    int sq[EPL];
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) {
+        s[q] = lane * EPL + q < E ? ordered_bits(x[q]) : 0u;  // 0: no expert
+        sq[q] = q;
+    }
+    // sorting network on (value descending, position ascending): a total order, so the
+    // network's result is the sorted list whatever the order of its exchanges
+    auto cx = [&](int i, int j) {
+        const bool sw = s[j] > s[i] || (s[j] == s[i] && sq[j] < sq[i]);
+        const uint32_t si = s[i], sj = s[j];
+        const int qi = sq[i], qj = sq[j];
+        s[i] = sw ? sj : si;
+        s[j] = sw ? si : sj;
+        sq[i] = sw ? qj : qi;
+        sq[j] = sw ? qi : qj;
+    };
+    if constexpr (EPL == 2) cx(0, 1);
+    if constexpr (EPL == 4) {
+        cx(0, 1);
+        cx(2, 3);
+        cx(0, 2);
+        cx(1, 3);
+        cx(1, 2);
+    }
+#pragma unroll
+    for (int j = 0; j < kRouteMaxK; ++j) {
+        if (j < k) {
+            // m >= 1: k <= E leaves an unretired expert in every round
+            const uint32_t m = wave_max_u32(s[0]);
+            const int wl = __builtin_ctzll(__builtin_amdgcn_ballot_w64(s[0] == m));
+            const int e = wl * EPL + __builtin_amdgcn_readlane(sq[0], wl);
+            const bool mine = lane == wl;
+#pragma unroll
+            for (int q = 0; q + 1 < EPL; ++q) {
+                s[q] = mine ? s[q + 1] : s[q];
+                sq[q] = mine ? sq[q + 1] : sq[q];
+            }
+            s[EPL - 1] = mine ? 0u : s[EPL - 1];
+            if (j == 0) top_o = m;
+            if (lane == j) {
+                my_e = e;
+                my_o = m;
+            }
+        }
+    }
+    my_v = from_ordered_bits(my_o);
+    top = from_ordered_bits(top_o);
+}
+
+// Top-k with experts strided over the lanes (lane l holds experts q*64 + l): each round takes
+// the wave maximum of the lanes' maxima, then one ballot per logit register finds the lowest
+// expert id holding it (the first register with a match, then its lowest lane), which is
+// retired.  Used where a lane holds too many logits to sort.
+template <int EPL>
+__device__ __forceinline__ void select_strided(const float (&x)[EPL], int lane, int E, int k,
+                                               int& my_e, float& my_v, float& top) {
+    uint32_t o[EPL], my_o = 0, top_o = 0;
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) o[q] = q * kWave + lane < E ? ordered_bits(x[q]) : 0u;
+#pragma unroll
+    for (int j = 0; j < kRouteMaxK; ++j) {
+        if (j < k) {
+            uint32_t lm = o[0];
+#pragma unroll
+            for (int q = 1; q < EPL; ++q) lm = umax(lm, o[q]);
+            const uint32_t m = wave_max_u32(lm);
+            int wq = 0;
+            uint64_t hit = 0;
+#pragma unroll
+            for (int q = EPL - 1; q >= 0; --q) {
+                const uint64_t bq = __builtin_amdgcn_ballot_w64(o[q] == m);
+                if (bq) {
+                    wq = q;
+                    hit = bq;
+                }
+            }
+            const int wl = __builtin_ctzll(hit);
+#pragma unroll
+            for (int q = 0; q < EPL; ++q)
+                if (q == wq && lane == wl) o[q] = 0u;  // retired
+            if (j == 0) top_o = m;
+            if (lane == j) {
+                my_e = wq * kWave + wl;
+                my_o = m;
+            }
+        }
+    }
+    my_v = from_ordered_bits(my_o);
+    top = from_ordered_bits(top_o);
+}
+
+// EPL: logits per lane, E <= 64 * EPL.  VEC: vector loads of the logits (see load_logits).
+template <int EPL, bool VEC>
 __global__ void __launch_bounds__(kRouteWaves * kWave) route_select_kernel(const RouteArgs a) {
     extern __shared__ uint16_t route_lds[];
     const int lane = threadIdx.x & (kWave - 1);
@@ -138,49 +268,17 @@ __global__ void __launch_bounds__(kRouteWaves * kWave) route_select_kernel(const
     for (int e = lane; e < E; e += kWave) mycnt[e] = 0;
 
     // --- top-k and softmax, one token at a time; the next token's logits are in flight ---
+    constexpr bool kLaneMajor = EPL <= kSortedMaxEpl;
     float x[EPL], xn[EPL];
-    if (ntok > 0) load_logits(x, a.logits + tw0 * E, E, lane);
+    if (ntok > 0) load_logits<EPL, kLaneMajor, VEC>(x, a.logits + tw0 * E, E, lane);
     for (int i = 0; i < ntok; ++i) {
         const int64_t t = tw0 + i;
         // the next token's logits (the last token re-reads its own row: no branch, in bounds)
-        load_logits(xn, a.logits + (i + 1 < ntok ? t + 1 : t) * E, E, lane);
-        uint32_t o[EPL];
-#pragma unroll
-        for (int q = 0; q < EPL; ++q) o[q] = q * kWave + lane < E ? ordered_bits(x[q]) : 0u;
+        load_logits<EPL, kLaneMajor, VEC>(xn, a.logits + (i + 1 < ntok ? t + 1 : t) * E, E, lane);
         int my_e = 0;
         float my_v = 0.0f, top = 0.0f;
-#pragma unroll
-        for (int j = 0; j < kRouteMaxK; ++j) {
-            if (j < k) {
-                uint32_t lm = o[0];
-#pragma unroll
-                for (int q = 1; q < EPL; ++q) lm = umax(lm, o[q]);
-                // m >= 1: k <= E leaves an unretired expert in every round
-                const uint32_t m = wave_max_u32(lm);
-                // the lowest expert id q*64 + lane holding m: the first register q with a match,
-                // then its lowest lane
-                int wq = 0;
-                uint64_t hit = 0;
-#pragma unroll
-                for (int q = EPL - 1; q >= 0; --q) {
-                    const uint64_t bq = __builtin_amdgcn_ballot_w64(o[q] == m);
-                    if (bq) {
-                        wq = q;
-                        hit = bq;
-                    }
-                }
-                const int wl = __builtin_ctzll(hit);
-#pragma unroll
-                for (int q = 0; q < EPL; ++q)
-                    if (q == wq && lane == wl) o[q] = 0u;  // retired
-                const float v = from_ordered_bits(m);
-                if (j == 0) top = v;
-                if (lane == j) {
-                    my_e = wq * kWave + wl;
-                    my_v = v;
-                }
-            }
-        }
+        if constexpr (kLaneMajor) select_sorted<EPL>(x, lane, E, k, my_e, my_v, top);
+        else select_strided<EPL>(x, lane, E, k, my_e, my_v, top);
         const float ex = expf(my_v - top);
         float sum = 0.0f;
         for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
