@@ -53,6 +53,7 @@ def _load():
         lib.oracle_moe_route.argtypes = [p, i64, i32, i32, p, p, p, p, p]
         lib.oracle_mxfp4_quantize.argtypes = [p, i64, i32, p, p]
         lib.oracle_rmsnorm_mxfp4_quantize.argtypes = [p, p, f32, p, p, i64, i32]
+        lib.oracle_rmsnorm_f32_mxfp4_quantize.argtypes = [p, p, f32, p, p, i64, i32]
         lib.oracle_bf16_round.argtypes = [p, p, i64]
         lib.oracle_bf16_round.restype = None
         _lib = lib
@@ -242,6 +243,22 @@ def rmsnorm_mxfp4_quantize(x, gamma, eps):
     sc = np.empty((T, H // 32), np.uint8)
     lib.oracle_rmsnorm_mxfp4_quantize(px, pg, float(eps), q.ctypes.data_as(ctypes.c_void_p),
                                       sc.ctypes.data_as(ctypes.c_void_p), T, H)
+    return q, sc
+
+
+def rmsnorm_f32_mxfp4_quantize(r, gamma, eps):
+    """RMSNorm of float32 rows r [T, H] (the finalize's residual_out) with gamma, rounded to
+    float32, then MXFP4: the finalize's MXFP4 epilogue.  Returns (q, scales) as above."""
+    lib = _load()
+    ra, pr = _c(r, np.float32)
+    g, pg = _c(gamma, np.uint16)
+    T, H = ra.shape
+    if H % 32:
+        raise ValueError("H must be a multiple of 32")
+    q = np.empty((T, H // 2), np.uint8)
+    sc = np.empty((T, H // 32), np.uint8)
+    lib.oracle_rmsnorm_f32_mxfp4_quantize(pr, pg, float(eps), q.ctypes.data_as(ctypes.c_void_p),
+                                          sc.ctypes.data_as(ctypes.c_void_p), T, H)
     return q, sc
 
 

@@ -375,6 +375,26 @@ int oracle_rmsnorm_mxfp4_quantize(const uint16_t* x, const uint16_t* gamma, floa
 }
 
 /*
+ * The same on fp32 rows (the finalize's residual_out): the MXFP4 epilogue of the finalize,
+ * whose normalised output is quantised instead of rounded to bf16.
+ *     y = fp32(r * rms_scale(r) * gamma);   (q, scales) = mxfp4(y)
+ */
+int oracle_rmsnorm_f32_mxfp4_quantize(const float* r, const uint16_t* gamma, float eps,
+                                      uint8_t* q, uint8_t* scales, int64_t T, int32_t H) {
+    double* v = (double*)malloc(sizeof(double) * (size_t)(H > 0 ? H : 1));
+    if (!v) return -2;
+    for (int64_t t = 0; t < T; ++t) {
+        const float* rt = r + t * (int64_t)H;
+        double s = rms_scale_f32(rt, H, eps);
+        for (int32_t h = 0; h < H; ++h)
+            v[h] = (double)(float)((double)rt[h] * s * bf16_value(gamma[h]));
+        mx_quantize_row(v, H, q + t * (int64_t)(H / 2), scales + t * (int64_t)(H / 32));
+    }
+    free(v);
+    return 0;
+}
+
+/*
  * Per-head RMSNorm with a sigmoid gate (same page, section 1.2): every head of every token
  * is normalised over its D values with one gamma[D] shared by all heads, then multiplied by
  * the sigmoid of the gate element.

@@ -488,6 +488,24 @@ def test_rmsnorm_mxfp4_scale_invariance_and_brute_force():
     assert np.all((np.abs(dec - y) <= 0.5 * step * 1.0001) | (np.abs(y) / X > 6))
 
 
+def test_rmsnorm_f32_mxfp4_agrees_with_the_bf16_form_on_bf16_values():
+    # bf16 values widen exactly, so the fp32-row form must give the same codes; and on rows of
+    # +-c it gives the saturated closed form of the golden example at any scale c
+    d = workloads.make_gated_inputs(5, 1024, seed=53)
+    q1, s1 = oracle.rmsnorm_mxfp4_quantize(d["x"], d["gamma"], 1e-6)
+    q2, s2 = oracle.rmsnorm_f32_mxfp4_quantize(f32(d["x"]), d["gamma"], 1e-6)
+    assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
+    g = json.load(open(GOLDEN))["rmsnorm_mxfp4_quantize"]
+    r = np.tile([3.0, -3.0], 16).astype(np.float32)[None] * np.float32(1024)
+    q, sc = oracle.rmsnorm_f32_mxfp4_quantize(r, workloads.to_bf16_bits(np.ones(32, np.float32)),
+                                              0.0)
+    # eps = 0: |y| = 1 exactly, floor(log2) = 0, e = -2, y / 2^-2 = 4: code 6 (and 14)
+    assert q[0].tolist() == [0xE6] * 16 and sc[0].tolist() == [125]
+    q, sc = oracle.rmsnorm_f32_mxfp4_quantize(r, workloads.to_bf16_bits(np.ones(32, np.float32)),
+                                              g["eps"])
+    assert q[0].tolist() == [0xE6] * 16 and sc[0].tolist() == [125]  # eps 1e-6 is invisible at 3072
+
+
 # ----------------------------------------------------------------------------- gated
 
 
