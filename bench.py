@@ -45,19 +45,21 @@ PROFILES = os.path.join(ROOT, "profiles")
 _NORM_SOURCES = ["mf_device.h", "row_norm.h", "norm_kernels.h", "api_util.h", "row_shape.h",
                  "norm_api.hip"]
 KERNEL_SOURCES = {
-    "finalize": ["mf_device.h", "row_norm.h", "finalize_kernel.h", "api_util.h", "row_shape.h",
-                 "mf_api.hip"],
-    "ep_partial": ["mf_device.h", "row_norm.h", "finalize_kernel.h", "api_util.h", "row_shape.h",
-                   "mf_api.hip"],
-    "ep_combine": ["mf_device.h", "row_norm.h", "finalize_kernel.h", "api_util.h", "row_shape.h",
-                   "mf_api.hip"],
+    "finalize": ["mf_device.h", "row_norm.h", "finalize_kernel.h", "mx_device.h", "api_util.h",
+                 "row_shape.h", "mf_api.hip"],
+    "ep_partial": ["mf_device.h", "row_norm.h", "finalize_kernel.h", "mx_device.h", "api_util.h",
+                   "row_shape.h", "mf_api.hip"],
+    "finalize_mx": ["mf_device.h", "row_norm.h", "finalize_kernel.h", "mx_device.h", "api_util.h",
+                    "row_shape.h", "mf_api.hip"],
+    "ep_combine": ["mf_device.h", "row_norm.h", "finalize_kernel.h", "mx_device.h", "api_util.h",
+                   "row_shape.h", "mf_api.hip"],
     "gated": _NORM_SOURCES,
     "gated_next": _NORM_SOURCES,
     "per_head": _NORM_SOURCES,
     "copy": _NORM_SOURCES,
     "route": ["mf_device.h", "route_kernels.h", "api_util.h", "route_api.hip"],
-    "rmsnorm_mx": ["mf_device.h", "row_norm.h", "mx_kernels.h", "api_util.h", "row_shape.h",
-                   "mx_api.hip"],
+    "rmsnorm_mx": ["mf_device.h", "row_norm.h", "mx_device.h", "mx_kernels.h", "api_util.h",
+                   "row_shape.h", "mx_api.hip"],
 }
 
 
@@ -103,6 +105,9 @@ def algorithmic_bytes(d: dict) -> int:
     if kind == "rmsnorm_mx":
         T, H = d["T"], d["H"]
         return T * H * 2 + H * 2 + T * H // 2 + T * H // 32   # x, gamma in; codes, scales out
+    if kind == "finalize_mx":
+        T, H, k = d["T"], d["H"], d["k"]
+        return T * (k * H * 2 + H * 4 + H * 4 + H // 2 + H // 32 + k * 8) + H * 2
     if kind == "ep_partial":
         # local rows read, every idx read, local weights read, the fp32 partial written
         T, H, k = d["T"], d["H"], d["k"]
@@ -163,6 +168,13 @@ def upload(d: dict, dev):
                     gamma=up(d["gamma"], True),
                     res_out=torch.empty((T, H), dtype=torch.float32, device=dev),
                     out=torch.empty((T, H), dtype=torch.bfloat16, device=dev))
+    if kind == "finalize_mx":
+        T, H = d["T"], d["H"]
+        return dict(rows=up(d["expert_rows"], True), idx=up(d["idx"]), w=up(d["weights"]),
+                    res=up(d["residual"]), gamma=up(d["gamma"], True),
+                    res_out=torch.empty((T, H), dtype=torch.float32, device=dev),
+                    q=torch.empty((T, H // 2), dtype=torch.uint8, device=dev),
+                    sc=torch.empty((T, H // 32), dtype=torch.uint8, device=dev))
     if kind == "rmsnorm_mx":
         T, H = d["T"], d["H"]
         return dict(x=up(d["x"], True), gamma=up(d["gamma"], True),
@@ -215,6 +227,10 @@ def launcher(d: dict, g: dict):
         return lambda: mf.mf_gated_residual_rmsnorm(g["x"], g["gate"], g["res"], g["gamma"],
                                                     d["eps"], residual_out=g["res_out"],
                                                     out=g["out"])
+    if kind == "finalize_mx":
+        return lambda: mf.mf_moe_finalize_mxfp4(g["rows"], g["idx"], g["w"], g["res"], g["gamma"],
+                                                d["eps"], residual_out=g["res_out"], q=g["q"],
+                                                scales=g["sc"])
     if kind == "rmsnorm_mx":
         return lambda: mf.mf_rmsnorm_mxfp4_quantize(g["x"], g["gamma"], d["eps"], q=g["q"],
                                                     scales=g["sc"])
@@ -243,7 +259,7 @@ def launcher(d: dict, g: dict):
 def launch_config(name: str, d: dict) -> dict:
     import finalize_residual_rmsnorm_amd as mf
     kind = d["kind"]
-    if kind in ("finalize", "ep_partial"):
+    if kind in ("finalize", "ep_partial", "finalize_mx"):
         pe = d.get("expert_gamma") is not None
         return mf.mf_launch_shape(mf.KIND_FINALIZE_PER_EXPERT if pe else mf.KIND_FINALIZE,
                                   d["T"], d["H"], d["k"])
@@ -286,6 +302,10 @@ def cpu_baseline(d: dict, target_cpu_s: float = 15.0, max_threads: int = 16) -> 
             oracle.moe_route(d["logits"][lo:hi], d["k"])
         elif kind == "rmsnorm_mx":
             oracle.rmsnorm_mxfp4_quantize(d["x"][lo:hi], d["gamma"], d["eps"])
+        elif kind == "finalize_mx":
+            r, _ = oracle.moe_finalize(d["expert_rows"], d["idx"][lo:hi], d["weights"][lo:hi],
+                                       d["residual"][lo:hi], d["gamma"], d["eps"])
+            oracle.rmsnorm_f32_mxfp4_quantize(r, d["gamma"], d["eps"])
         elif kind == "ep_partial":
             oracle.moe_finalize_ep_partial(d["expert_rows"], d["idx"][lo:hi], d["weights"][lo:hi],
                                            d["eps"])
@@ -336,7 +356,7 @@ def main() -> int:
                     choices=["finalize_prefill", "finalize_decode_per_expert", "finalize_tiny",
                              "gated_residual_rmsnorm", "gated_residual_next_rmsnorm",
                              "rmsnorm_sigmoid_gate", "moe_route_prefill", "finalize_ep_partial",
-                             "finalize_ep_combine", "rmsnorm_mxfp4",
+                             "finalize_ep_combine", "rmsnorm_mxfp4", "finalize_prefill_mxfp4",
                              "moe_route_decode", "stream_copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

@@ -23,7 +23,7 @@ __all__ = [
     "mf_moe_route", "mf_moe_route_supported", "mf_moe_route_workspace_bytes",
     "mf_gated_residual_next_rmsnorm", "mf_gated_residual_next_rmsnorm_supported",
     "mf_moe_finalize_ep_partial", "mf_moe_finalize_ep_combine", "mf_mxfp4_quantize",
-    "mf_rmsnorm_mxfp4_quantize", "mf_mxfp4_supported", "LIB_PATH",
+    "mf_rmsnorm_mxfp4_quantize", "mf_mxfp4_supported", "mf_moe_finalize_mxfp4", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmf.so")
@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
             "mf_mxfp4_quantize": [p, i64, i32, p, p, p],
             "mf_rmsnorm_mxfp4_quantize": [p, p, f32, p, p, i64, i32, p],
             "mf_mxfp4_supported": [i32],
+            "mf_moe_finalize_mxfp4": [p, i64, p, p, p, p, p, f32, p, p, i64, i32, i32, p],
             "mf_moe_route_supported": [i32, i32],
             "mf_moe_route_workspace_bytes": [i64, i32, i32],
         }
@@ -386,3 +387,27 @@ def mf_rmsnorm_mxfp4_quantize(x: torch.Tensor, gamma: torch.Tensor, eps: float =
                                          _stream(stream, x.device))
     _check("mf_rmsnorm_mxfp4_quantize", st)
     return q, scales
+
+
+def mf_moe_finalize_mxfp4(expert_rows: torch.Tensor, idx: torch.Tensor, weights: torch.Tensor,
+                          residual: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, *,
+                          residual_out: torch.Tensor | None = None, q: torch.Tensor | None = None,
+                          scales: torch.Tensor | None = None, stream=None):
+    """MoE finalize + residual add + RMSNorm with the output quantised to MXFP4.
+    Returns (q uint8 [T, H/2], scales uint8 [T, H/32], residual_out fp32 [T, H])."""
+    T, k = idx.shape
+    num_rows, H = expert_rows.shape
+    dev = expert_rows.device
+    if residual_out is None:
+        residual_out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    q, scales = _mx_outputs(T, H, dev, q, scales)
+    st = lib().mf_moe_finalize_mxfp4(
+        _dev(expert_rows, torch.bfloat16, "expert_rows"), num_rows, _dev(idx, torch.int32, "idx"),
+        _dev(weights, torch.float32, "weights", (T, k)),
+        _dev(residual, torch.float32, "residual", (T, H)),
+        _dev(residual_out, torch.float32, "residual_out", (T, H)),
+        _dev(gamma, torch.bfloat16, "gamma", (H,)), float(eps),
+        _dev(q, torch.uint8, "q", (T, H // 2)), _dev(scales, torch.uint8, "scales", (T, H // 32)),
+        T, H, k, _stream(stream, dev))
+    _check("mf_moe_finalize_mxfp4", st)
+    return q, scales, residual_out

@@ -32,6 +32,7 @@
 //    order from +0, then the residual add and the final RMSNorm as above.
 #pragma once
 
+#include "mx_device.h"
 #include "row_norm.h"
 
 namespace mf {
@@ -46,6 +47,8 @@ struct FinalizeArgs {
     float* residual_out;         // [T, H], may equal residual
     const uint16_t* gamma;       // bf16 [H]
     uint16_t* out;               // bf16 [T, H]
+    uint8_t* q;                  // MXFP4 output: codes [T, H/2] (OUT_MX only)
+    uint8_t* scales;             // MXFP4 output: scales [T, H/32] (OUT_MX only)
     int64_t T;
     int64_t num_rows;
     int32_t H;
@@ -168,11 +171,18 @@ __device__ __forceinline__ void consume_batch(const GatherBatch<VPL, JB, PER_EXP
 // KC: the top-k fixed at compile time (8), or 0 for a runtime k.  PARTIAL: this GPU's share
 // of the expert-parallel split (slots with idx < 0 skipped; the fp32 accumulator is stored to
 // residual_out, which then holds the [T, H] partial; residual, gamma and out are unused).
-template <int VPL, int KC, bool PER_EXPERT, int TAIL, bool PARTIAL = false>
+// OUT_MX: the MXFP4 epilogue: the normalised output is quantised to MXFP4 (q, scales) instead
+// of rounded to bf16 (page "FlashInfer: fused norms and TP/EP MoE for Muse-Spark-Open",
+// PR #6544, section 2.3: RMSNorm + block-scaled FP4 quantisation; the OCP MXFP4 format).
+template <int VPL, int KC, bool PER_EXPERT, int TAIL, bool PARTIAL = false, bool OUT_MX = false>
 __global__ void __launch_bounds__(finalize_block_max(PER_EXPERT))
-__attribute__((amdgpu_waves_per_eu(finalize_min_waves(VPL, PER_EXPERT), 8)))
+__attribute__((amdgpu_waves_per_eu(OUT_MX && KC == 0 ? (VPL == 1 ? 6 : 4)
+                                                     : finalize_min_waves(VPL, PER_EXPERT), 8)))
 moe_finalize_kernel(const FinalizeArgs a) {
-    constexpr int JB = batch_rows(VPL, KC, PER_EXPERT);
+    // (the MXFP4 epilogue keeps its store addresses live across the loop: with two or more
+    // slots and a runtime k, half the batch keeps it out of scratch)
+    constexpr int JB = OUT_MX && VPL >= 2 && KC == 0 ? (batch_rows(VPL, KC, PER_EXPERT) + 1) / 2
+                                                     : batch_rows(VPL, KC, PER_EXPERT);
     // With small row slices the residual and gamma ride along with the first batch.
     constexpr bool EARLY = VPL <= 2;
     extern __shared__ float lds[];
@@ -235,7 +245,14 @@ moe_finalize_kernel(const FinalizeArgs a) {
             acc[s][4 + i] = rv[s][1][i] + acc[s][4 + i];
         }
     store_residual(acc, sl, a.residual_out + m.t * H);
-    rmsnorm_store(acc, g, sl, a.out + m.t * H, H, a.eps, L, m);
+    if constexpr (OUT_MX) {
+        float ss[1] = {lane_sumsq(acc, sl)};
+        token_sum<1>(ss, L, m);
+        const float inv = 1.0f / __builtin_sqrtf(ss[0] / (float)H + a.eps);
+        mx_store_normed(acc, g, sl, inv, m.lane, a.q + m.t * (H / 2), a.scales + m.t * (H / 32));
+    } else {
+        rmsnorm_store(acc, g, sl, a.out + m.t * H, H, a.eps, L, m);
+    }
 }
 
 // The token owner's combine of the expert-parallel split.

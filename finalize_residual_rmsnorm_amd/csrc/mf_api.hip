@@ -36,12 +36,12 @@ RowShape finalize_shape(int64_t T, int32_t H, int32_t k, bool per_expert) {
     return s;
 }
 
-template <int VPL, int KC, bool PE, bool PARTIAL>
+template <int VPL, int KC, bool PE, bool PARTIAL, bool OUT_MX = false>
 const void* finalize_fn(int tail) {
     switch (tail) {
-        case kRowFull: return reinterpret_cast<const void*>(&moe_finalize_kernel<VPL, KC, PE, kRowFull, PARTIAL>);
-        case kRowWhole: return reinterpret_cast<const void*>(&moe_finalize_kernel<VPL, KC, PE, kRowWhole, PARTIAL>);
-        default: return reinterpret_cast<const void*>(&moe_finalize_kernel<VPL, KC, PE, kRowRagged, PARTIAL>);
+        case kRowFull: return reinterpret_cast<const void*>(&moe_finalize_kernel<VPL, KC, PE, kRowFull, PARTIAL, OUT_MX>);
+        case kRowWhole: return reinterpret_cast<const void*>(&moe_finalize_kernel<VPL, KC, PE, kRowWhole, PARTIAL, OUT_MX>);
+        default: return reinterpret_cast<const void*>(&moe_finalize_kernel<VPL, KC, PE, kRowRagged, PARTIAL, OUT_MX>);
     }
 }
 
@@ -85,6 +85,25 @@ const void* finalize_kernel_for_mode(const RowShape& s, int k, bool per_expert) 
 const void* finalize_kernel_for(const RowShape& s, int k, bool per_expert, bool partial = false) {
     return partial ? finalize_kernel_for_mode<true>(s, k, per_expert)
                    : finalize_kernel_for_mode<false>(s, k, per_expert);
+}
+
+// The MXFP4 epilogue is built for the plain finalize (no per-expert norm).
+template <int VPL>
+const void* finalize_mx_fn(int tail, int k) {
+    if constexpr (uses_compiled_topk(VPL, false)) {
+        if (k == kCompiledTopK) return finalize_fn<VPL, kCompiledTopK, false, false, true>(tail);
+    }
+    return finalize_fn<VPL, 0, false, false, true>(tail);
+}
+
+const void* finalize_mx_kernel_for(const RowShape& s, int k) {
+    switch (s.vpl) {
+        case 1: return finalize_mx_fn<1>(s.tail, k);
+        case 2: return finalize_mx_fn<2>(s.tail, k);
+        case 3: return finalize_mx_fn<3>(s.tail, k);
+        case 4: return finalize_mx_fn<4>(s.tail, k);
+        default: return nullptr;
+    }
 }
 
 template <int VPL>
@@ -190,6 +209,64 @@ int mf_moe_finalize(const uint16_t* expert_rows, int64_t num_rows, const int32_t
     a.k = k;
     a.num_experts = per_expert ? num_experts : 0;
     a.eps = eps;
+    a.q = nullptr;
+    a.scales = nullptr;
+    void* args[] = {&a};
+    return hip_status(hipLaunchKernel(fn, dim3((unsigned)s.grid), dim3(s.block), args, s.lds,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+int mf_moe_finalize_mxfp4(const uint16_t* expert_rows, int64_t num_rows, const int32_t* idx,
+                          const float* weights, const float* residual, float* residual_out,
+                          const uint16_t* gamma, float eps, uint8_t* q, uint8_t* scales,
+                          int64_t T, int32_t H, int32_t k, void* stream) {
+    if (T < 0 || num_rows < 0) return MF_ERR_SHAPE;
+    if (!mf_moe_finalize_supported(H, k, 0) || H % 32 != 0) return MF_ERR_UNSUPPORTED;
+    if (T == 0) return MF_OK;
+    const RowShape s = finalize_shape(T, H, k, false);
+    if (!grid_fits(s.grid, s.block)) return MF_ERR_SHAPE;
+    const void* fn = finalize_mx_kernel_for(s, k);
+    if (!fn || s.block > finalize_block_max(false)) return MF_ERR_UNSUPPORTED;
+    if (!expert_rows || !idx || !weights || !residual || !residual_out || !gamma || !q || !scales)
+        return MF_ERR_NULL;
+    if (num_rows < 1) return MF_ERR_SHAPE;
+    if (!eps_ok(eps)) return MF_ERR_VALUE;
+    if (!aligned(expert_rows, 16) || !aligned(residual, 16) || !aligned(residual_out, 16) ||
+        !aligned(gamma, 16) || !aligned(q, 4) || !aligned(idx, 4) || !aligned(weights, 4))
+        return MF_ERR_ALIGN;
+    const size_t th = size_t(T) * H;
+    const size_t tk = size_t(T) * k;
+    if (residual_out != residual && overlap(residual_out, th * 4, residual, th * 4))
+        return MF_ERR_ALIAS;
+    const void* ins[] = {expert_rows, idx, weights, gamma, residual};
+    const size_t in_bytes[] = {size_t(num_rows) * H * 2, tk * 4, tk * 4, size_t(H) * 2, th * 4};
+    for (int i = 0; i < 5; ++i) {
+        if ((i < 4 && overlap(residual_out, th * 4, ins[i], in_bytes[i])) ||
+            overlap(q, th / 2, ins[i], in_bytes[i]) || overlap(scales, th / 32, ins[i], in_bytes[i]))
+            return MF_ERR_ALIAS;
+    }
+    if (overlap(q, th / 2, residual_out, th * 4) || overlap(scales, th / 32, residual_out, th * 4) ||
+        overlap(q, th / 2, scales, th / 32))
+        return MF_ERR_ALIAS;
+
+    FinalizeArgs a;
+    a.rows = expert_rows;
+    a.idx = idx;
+    a.w = weights;
+    a.eids = nullptr;
+    a.egamma = nullptr;
+    a.residual = residual;
+    a.residual_out = residual_out;
+    a.gamma = gamma;
+    a.out = nullptr;
+    a.q = q;
+    a.scales = scales;
+    a.T = T;
+    a.num_rows = num_rows;
+    a.H = H;
+    a.k = k;
+    a.num_experts = 0;
+    a.eps = eps;
     void* args[] = {&a};
     return hip_status(hipLaunchKernel(fn, dim3((unsigned)s.grid), dim3(s.block), args, s.lds,
                                       reinterpret_cast<hipStream_t>(stream)));
@@ -240,6 +317,8 @@ int mf_moe_finalize_ep_partial(const uint16_t* expert_rows, int64_t num_rows,
     a.k = k;
     a.num_experts = per_expert ? num_experts : 0;
     a.eps = eps;
+    a.q = nullptr;
+    a.scales = nullptr;
     void* args[] = {&a};
     return hip_status(hipLaunchKernel(fn, dim3((unsigned)s.grid), dim3(s.block), args, s.lds,
                                       reinterpret_cast<hipStream_t>(stream)));

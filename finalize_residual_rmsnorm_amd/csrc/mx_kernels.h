@@ -18,40 +18,10 @@
 //    fill the lane's 32-bit word of codes.
 #pragma once
 
+#include "mx_device.h"
 #include "row_norm.h"
 
 namespace mf {
-
-// The E8M0 scale code of a block from its maximum magnitude (>= 0), and the scale as an fp32
-// power of two (2^-127, code 0, is a denormal: the conversion takes it as 2^-127).
-__device__ __forceinline__ uint32_t mx_scale_code(float amax) {
-    const int be = int((__float_as_uint(amax) >> 23) & 0xFFu);
-    return uint32_t(be > 2 ? be - 2 : 0);
-}
-
-__device__ __forceinline__ float mx_scale_value(uint32_t code) {
-    return __uint_as_float(code > 0 ? code << 23 : 0x00400000u);
-}
-
-// Maximum of |v| over the lane's 8 values and its quad (lanes 4q .. 4q+3, all active).
-__device__ __forceinline__ float mx_block_max(const float (&v)[8]) {
-    float m = __builtin_fabsf(v[0]);
-#pragma unroll
-    for (int i = 1; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
-    m = __builtin_fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
-    m = __builtin_fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
-    return m;
-}
-
-// The lane's 8 codes, value 2i in the low nibble of byte i.
-__device__ __forceinline__ uint32_t mx_pack8(const float (&v)[8], float scale) {
-    uint32_t w = 0;
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], scale, 0);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], scale, 2);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], scale, 3);
-    return w;
-}
 
 // ---------------------------------------------------------------------------------------
 // fp32 [T, H] -> codes [T, H/2], scales [T, H/32] (H % 32 == 0).  Flat over 8-value chunks:
@@ -122,21 +92,7 @@ rmsnorm_mxfp4_kernel(const RmsMxArgs a) {
     TokenLds L = token_lds(lds, m.wpt, 1);
     token_sum<1>(ss, L, m);
     const float inv = 1.0f / __builtin_sqrtf(ss[0] / (float)H + a.eps);
-    uint8_t* qr = a.q + m.t * (H / 2);
-    uint8_t* sr = a.scales + m.t * (H / 32);
-#pragma unroll
-    for (int s = 0; s < VPL; ++s) {
-        float g[8], y[8];
-        widen8(gm[s], g);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = (x[s][i] * inv) * g[i];
-        const uint32_t code = mx_scale_code(mx_block_max(y));
-        const uint32_t w = mx_pack8(y, mx_scale_value(code));
-        if (sl.sval[s]) {
-            *at<uint32_t>(qr, sl.eoff[s] / 2u) = w;
-            if ((m.lane & 3) == 0) sr[sl.eoff[s] / 32u] = uint8_t(code);
-        }
-    }
+    mx_store_normed(x, gm, sl, inv, m.lane, a.q + m.t * (H / 2), a.scales + m.t * (H / 32));
 }
 
 }  // namespace mf

@@ -86,6 +86,20 @@ int mf_moe_finalize(const uint16_t* expert_rows, int64_t num_rows, const int32_t
                     int64_t T, int32_t H, int32_t k, void* stream);
 
 /*
+ * mf_moe_finalize with an MXFP4 epilogue ([PR6544] section 2.3: RMSNorm + block-scaled FP4
+ * quantisation; the MXFP4 format as for mf_mxfp4_quantize below): residual_out as in
+ * mf_moe_finalize, and instead of the bf16 out the normalised row
+ *   y = fp32((residual_out * (mean(residual_out^2) + eps)^-1/2) * gamma)
+ * quantised to MXFP4: q uint8 [T, H/2] (4-byte aligned) and scales uint8 [T, H/32].  The plain
+ * finalize only (no per-expert norm); H % 32 == 0; other arguments and checks as
+ * mf_moe_finalize's.
+ */
+int mf_moe_finalize_mxfp4(const uint16_t* expert_rows, int64_t num_rows, const int32_t* idx,
+                          const float* weights, const float* residual, float* residual_out,
+                          const uint16_t* gamma, float eps, uint8_t* q, uint8_t* scales,
+                          int64_t T, int32_t H, int32_t k, void* stream);
+
+/*
  * The expert-parallel split of the finalize ([PR6544] section 2.4: finalize + RMSNorm +
  * all-reduce, where the slots of non-local experts skip normalisation; [PR4730] section 2: the
  * all-reduce's sum fused with the residual add and RMSNorm).  Between the two calls the

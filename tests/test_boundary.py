@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported():
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     L = ctypes.CDLL(mf.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -146,6 +146,22 @@ def test_mxfp4_rejects_bad_arguments():
     assert r(A, D, 1e-6, B, A + 100, 4, 64, None) == ALIAS
     assert r(A, D, 1e-6, B, C, 0, 64, None) == OK
     assert mf.mf_mxfp4_supported(7168) and not mf.mf_mxfp4_supported(7176)
+
+
+def test_finalize_mxfp4_rejects_bad_arguments():
+    f = lambda **kw: mf.lib().mf_moe_finalize_mxfp4(*[kw.get(n, v) for n, v in (
+        ("rows", A), ("num_rows", 32), ("idx", B), ("w", C), ("res", D), ("res_out", E_),
+        ("gamma", F), ("eps", 1e-6), ("q", G), ("sc", H_), ("T", 16), ("H", 1024), ("k", 2))],
+        None)
+    assert f(T=-1) == SHAPE
+    assert f(H=1032) == UNSUP           # a multiple of 8 but not of 32
+    assert f(k=0) == UNSUP
+    assert f(q=None) == NULL and f(sc=None) == NULL and f(rows=None) == NULL
+    assert f(num_rows=0) == SHAPE
+    assert f(eps=float("nan")) == VALUE
+    assert f(q=G + 2) == ALIGN and f(res_out=E_ + 4) == ALIGN
+    assert f(q=A) == ALIAS and f(sc=E_ + 8) == ALIAS and f(sc=G + 100) == ALIAS
+    assert f(T=0) == OK
 
 
 def test_finalize_zero_tokens_is_a_no_op():

@@ -10,6 +10,9 @@ Bars:
     maximum within a relative band of 2^-20 of the oracle's, and every decoded value one its
     rule gives for a value within that band of the oracle's; and >= 99.9% of all codes and
     scales are bit-identical.
+  - mf_moe_finalize_mxfp4: residual_out bit-identical to the oracle's finalize (the same fp32
+    FMA chain as mf_moe_finalize); codes and scales to the band bar above, against the oracle's
+    RMSNorm + MXFP4 of that fp32 residual.
 Each case prints its name and sizes before it runs.
 """
 import json
@@ -120,9 +123,15 @@ def nearest(r):
 def check_rms_mx(x, gamma, eps):
     q, sc = rms_mx_gpu(x, gamma, eps)
     q_ref, sc_ref = oracle.rmsnorm_mxfp4_quantize(x, gamma, eps)
-    T, H = x.shape
+    check_band(q, sc, q_ref, sc_ref, workloads.bf16_bits_to_f32(x), gamma, eps)
+
+
+def check_band(q, sc, q_ref, sc_ref, xf, gamma, eps):
+    """q, sc from the GPU against the oracle's (q_ref, sc_ref) for the RMSNorm of the fp32 rows
+    xf with gamma: the band bar of the module docstring."""
+    T, H = xf.shape
     # the oracle's fp32 normalised value, and a band around it
-    xd = workloads.bf16_bits_to_f32(x).astype(np.float64)
+    xd = xf.astype(np.float64)
     s = 1.0 / np.sqrt((xd * xd).mean(axis=1, keepdims=True) + eps)
     y = (xd * s * workloads.bf16_bits_to_f32(gamma)).astype(np.float32).astype(np.float64)
     lo, hi = y * (1 - BAND), y * (1 + BAND)
@@ -165,3 +174,67 @@ def test_rmsnorm_mxfp4_workload_full_size():
     d = workloads.make_inputs("rmsnorm_mxfp4")
     say("rmsnorm mxfp4 workload T=4096 H=8192")
     check_rms_mx(d["x"], d["gamma"], d["eps"])
+
+
+def up(a, bf16=False):
+    a = np.ascontiguousarray(a)
+    t = torch.from_numpy(a.view(np.int16) if bf16 else a)
+    if bf16:
+        t = t.view(torch.bfloat16)
+    return t.to(DEV)
+
+
+def finalize_mx_gpu(d, in_place=False):
+    res = up(d["residual"])
+    q, sc, r = mf.mf_moe_finalize_mxfp4(up(d["expert_rows"], True), up(d["idx"]),
+                                        up(d["weights"]), res, up(d["gamma"], True), d["eps"],
+                                        residual_out=res if in_place else None)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), sc.cpu().numpy(), r.cpu().numpy()
+
+
+def check_finalize_mx(d, rows=None, in_place=False):
+    q, sc, r = finalize_mx_gpu(d, in_place)
+    sel = slice(None) if rows is None else rows
+    r_ref, _ = oracle.moe_finalize(d["expert_rows"], d["idx"][sel], d["weights"][sel],
+                                   d["residual"][sel], d["gamma"], d["eps"])
+    assert np.array_equal(r[sel].view(np.uint32), r_ref.view(np.uint32)), "residual_out differs"
+    q_ref, sc_ref = oracle.rmsnorm_f32_mxfp4_quantize(r_ref, d["gamma"], d["eps"])
+    check_band(q[sel], sc[sel], q_ref, sc_ref, r_ref, d["gamma"], d["eps"])
+
+
+@pytest.mark.parametrize("T,H,k,layout", [
+    (1, 32, 1, "random"), (17, 1024, 8, "random"), (33, 4128, 9, "random"),
+    (100, 7168, 8, "expert_grouped"), (5, 32768, 3, "random"), (64, 4096, 16, "random"),
+    (2049, 512, 4, "random"), (7, 12288, 32, "random"),
+])
+def test_finalize_mxfp4_matches_oracle(T, H, k, layout):
+    say(f"finalize mxfp4 T={T} H={H} k={k} layout={layout}")
+    d = workloads.make_finalize_inputs(T, H, E=max(16, k), k=k, seed=950 + T + H + k,
+                                       layout=layout)
+    check_finalize_mx(d)
+
+
+def test_finalize_mxfp4_in_place():
+    d = workloads.make_finalize_inputs(100, 7168, E=64, k=8, seed=960)
+    say("finalize mxfp4 in place: T=100 H=7168 k=8")
+    check_finalize_mx(d, in_place=True)
+
+
+def test_finalize_mxfp4_agrees_with_two_steps():
+    """The fused epilogue's residual_out equals mf_moe_finalize's, bit for bit."""
+    d = workloads.make_finalize_inputs(257, 7168, E=64, k=8, seed=961)
+    say("finalize mxfp4 vs finalize: T=257 H=7168 k=8")
+    _, _, r = finalize_mx_gpu(d)
+    _, r1 = mf.mf_moe_finalize(up(d["expert_rows"], True), up(d["idx"]), up(d["weights"]),
+                               up(d["residual"]), up(d["gamma"], True), d["eps"])
+    torch.cuda.synchronize()
+    assert np.array_equal(r.view(np.uint32), r1.cpu().numpy().view(np.uint32))
+
+
+def test_finalize_mxfp4_workload_full_size():
+    d = workloads.make_inputs("finalize_prefill_mxfp4")
+    rows = np.sort(np.random.default_rng(962).choice(d["T"], 1024, replace=False))
+    rows[0], rows[-1] = 0, d["T"] - 1
+    say("finalize mxfp4 workload T=16384 H=7168 k=8, 1024 sampled rows")
+    check_finalize_mx(d, rows=rows)

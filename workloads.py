@@ -76,6 +76,10 @@ WORKLOADS = {
     # The dual-output form: the same gated residual feeding this layer's and the next layer's
     # RMSNorm (two gammas), at the same fixed hidden size.
     "gated_residual_next_rmsnorm": dict(kind="gated", T=4096, H=8192, seed=8, dual=True),
+    # The prefill finalize with its output quantised to MXFP4 (same inputs as finalize_prefill).
+    "finalize_prefill_mxfp4": dict(kind="finalize", T=16384, H=7168, E=256, k=8, seed=3,
+                                   layout="expert_grouped", per_expert=False, residual_std=1.0,
+                                   mx_out=True),
     # RMSNorm + MXFP4 quantisation of bf16 rows at hidden size 8192.
     "rmsnorm_mxfp4": dict(kind="rmsnorm_mx", T=4096, H=8192, seed=11),
     # Per-head RMSNorm + sigmoid gate at its fixed head dim.
@@ -155,7 +159,7 @@ def unpermute_index(rng: np.random.Generator, expert_ids: np.ndarray, layout: st
 
 def make_finalize_inputs(T: int, H: int, E: int, k: int, seed: int, layout: str = "expert_grouped",
                          per_expert: bool = False, residual_std: float = 1.0, ep_ranks: int = 0,
-                         ep_rank: int = 0) -> dict:
+                         ep_rank: int = 0, mx_out: bool = False) -> dict:
     rng = np.random.default_rng(seed)
     expert_ids, w = draw_routing(rng, T, E, k)
     idx = unpermute_index(rng, expert_ids, layout)
@@ -167,6 +171,8 @@ def make_finalize_inputs(T: int, H: int, E: int, k: int, seed: int, layout: str 
              expert_gamma=None)
     if per_expert:
         d["expert_gamma"] = to_bf16_bits(1.0 + 0.1 * _normal_f32(rng, E * H)).reshape(E, H)
+    if mx_out:
+        d["kind"] = "finalize_mx"  # the same inputs; the output is quantised to MXFP4
     if ep_ranks:
         # one GPU's view under expert parallelism: expert e lives on rank e % ep_ranks, and the
         # slots of other ranks' experts are marked -1 (no draw: the same bytes otherwise)
