@@ -338,10 +338,30 @@ def cpu_baseline(d: dict, target_cpu_s: float = 15.0, max_threads: int = 16) -> 
         for _ in range(reps):
             list(ex.map(lambda s: run(*s), spans))
         dt = time.perf_counter() - t0
+    # one thread on one token block of the same size, for about a fifth of the target
+    one = spans[0][1] - spans[0][0]
+    reps1 = max(1, int(target_cpu_s / 5 / max(one * per_token, 1e-9)))
+    t0 = time.perf_counter()
+    for _ in range(reps1):
+        run(0, one)
+    dt1 = time.perf_counter() - t0
     what = f"the first {n} of {T} tokens" if n < T else f"all {T} tokens"
     return dict(value=n * reps / dt, unit="tokens/s", cores=min(threads, len(spans)), kind="oracle",
                 sample=f"{what} of the same inputs, {reps} pass(es), {len(spans)} threads over "
-                       f"token blocks, {dt:.1f} s wall")
+                       f"token blocks, {dt:.1f} s wall",
+                value_1_thread=one * reps1 / dt1,
+                sample_1_thread=f"the first {one} tokens, {reps1} pass(es), {dt1:.1f} s",
+                cpu_model=cpu_model())
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ------------------------------------------------------------------------------ main
