@@ -341,7 +341,7 @@ moe_finalize_combine_kernel(const CombineArgs a) {
         }
     store_residual(acc, sl, a.residual_out + row);
     TokenLds L = token_lds(lds, m.wpt, 1);
-    rmsnorm_store(acc, g, sl, a.out + row, H, a.eps, L, m);
+    rmsnorm_store<true>(acc, g, sl, a.out + row, H, a.eps, L, m);
 }
 
 }  // namespace mf

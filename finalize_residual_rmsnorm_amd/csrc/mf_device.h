@@ -52,6 +52,12 @@ template <class T>
 __device__ __forceinline__ T ld_stream(const T* p) { return __builtin_nontemporal_load(p); }
 template <class T>
 __device__ __forceinline__ void st_stream(T v, T* p) { __builtin_nontemporal_store(v, p); }
+// A load whose cache policy is a compile-time choice (nontemporal or default).
+template <bool NT, class T>
+__device__ __forceinline__ T ld_policy(const T* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {

@@ -161,10 +161,11 @@ __device__ __forceinline__ void load_gamma(u32x4 (&g)[VPL], const uint16_t* gamm
 
 // Final RMSNorm of a row held as r[VPL][8] (fp32) and the bf16 store of out:
 //   out = bf16((r * (sum(r^2)/H + eps)^-1/2) * gamma).
-// out is stored with the default cache policy: each wave instruction writes whole 128-byte
-// lines, and on MI355X that measured 4% faster for the finalize than a nontemporal store
-// (the half-line fp32 residual stores are the opposite: nontemporal is faster there).
-template <int VPL, int TAIL>
+// OUT_NT selects the cache policy of the out stores, which was measured per kernel on MI355X:
+// the finalize and the gated-residual norm are faster with the default policy (4% for the
+// finalize; each wave instruction writes whole 128-byte lines), the expert-parallel combine
+// 3% faster with nontemporal stores.
+template <bool OUT_NT = false, int VPL, int TAIL>
 __device__ __forceinline__ void rmsnorm_store(const float (&r)[VPL][8], const u32x4 (&g)[VPL],
                                               const Slots<VPL, TAIL>& sl, uint16_t* out_row,
                                               int H, float eps, TokenLds& L, const RowMap& m) {
@@ -180,7 +181,12 @@ __device__ __forceinline__ void rmsnorm_store(const float (&r)[VPL][8], const u3
         for (int i = 0; i < 4; ++i)
             o[i] = pack_bf16x2((r[s][2 * i] * inv) * gf[2 * i],
                                (r[s][2 * i + 1] * inv) * gf[2 * i + 1]);
-        if (sl.sval[s]) *at<u32x4>(out_row, sl.eoff[s] * 2u) = o;
+        if (sl.sval[s]) {
+            if constexpr (OUT_NT)
+                st_stream(o, at<u32x4>(out_row, sl.eoff[s] * 2u));
+            else
+                *at<u32x4>(out_row, sl.eoff[s] * 2u) = o;
+        }
     }
 }
 
