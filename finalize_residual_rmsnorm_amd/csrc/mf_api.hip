@@ -27,6 +27,14 @@ constexpr int kCompiledTopK = 8;
 
 constexpr bool uses_compiled_topk(int vpl, bool per_expert);
 
+// The combine runs at most 8 waves per token (two slots per wave at H = 7168): measured 2%
+// faster than 16 waves.  Rows too wide for 8 waves of kMaxVpl slots take 16.
+constexpr int kCombineWaves = 8;
+RowShape combine_shape(int64_t T, int32_t H) {
+    const RowShape s = row_shape(T, H, kCombineWaves, kMaxVpl);
+    return s.vpl <= kMaxVpl ? s : row_shape(T, H, kMaxWaves, kMaxVpl);
+}
+
 RowShape finalize_shape(int64_t T, int32_t H, int32_t k, bool per_expert) {
     RowShape s = per_expert ? row_shape(T, H, kMaxWavesPerExpert, kMaxVplPerExpert)
                             : row_shape(T, H, kMaxWaves, kMaxVpl);
@@ -330,7 +338,7 @@ int mf_moe_finalize_ep_combine(const float* partials, int32_t num_ranks, const f
     if (T < 0 || num_ranks < 1 || num_ranks > kMaxRanks) return MF_ERR_SHAPE;
     if (!row_width_supported(H)) return MF_ERR_UNSUPPORTED;
     if (T == 0) return MF_OK;
-    const RowShape s = row_shape(T, H, kMaxWaves, kMaxVpl);
+    const RowShape s = combine_shape(T, H);
     if (!grid_fits(s.grid, s.block)) return MF_ERR_SHAPE;
     const void* fn = combine_kernel_for(s);
     if (!fn) return MF_ERR_UNSUPPORTED;

@@ -16,7 +16,10 @@ namespace {
 
 using namespace mf;
 
-constexpr int kPerHeadGroupsPerWave = 2;
+// One group of 8 heads per wave and one wave per workgroup: measured 7% faster on MI355X than
+// two groups per wave in 4-wave workgroups (every other combination of 1-2 groups and 64-1024
+// threads was within 1% of the latter).
+constexpr int kPerHeadGroupsPerWave = 1;
 
 template <int VPL, bool DUAL>
 const void* gated_fn(int tail) {
@@ -136,8 +139,9 @@ int mf_rmsnorm_sigmoid_gate(const uint16_t* x, const uint16_t* gate, const uint1
     const int64_t nh = T * num_heads;
     const int64_t groups = (nh + kHeadsPerWaveLoad - 1) / kHeadsPerWaveLoad;
     const int64_t waves = (groups + G - 1) / G;
-    const int64_t blocks = (waves + 3) / 4;
-    if (!grid_fits(blocks, 256)) return MF_ERR_SHAPE;
+    constexpr int WPB = kPerHeadBlock / kWave;
+    const int64_t blocks = (waves + WPB - 1) / WPB;
+    if (!grid_fits(blocks, kPerHeadBlock)) return MF_ERR_SHAPE;
     if (!x || !gate || !gamma || !out) return MF_ERR_NULL;
     if (!eps_ok(eps)) return MF_ERR_VALUE;
     if (!aligned(x, 16) || !aligned(gate, 16) || !aligned(gamma, 16) || !aligned(out, 16))
@@ -156,7 +160,7 @@ int mf_rmsnorm_sigmoid_gate(const uint16_t* x, const uint16_t* gate, const uint1
     a.eps = eps;
     void* args[] = {&a};
     return hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&rmsnorm_sigmoid_gate_kernel<G>),
-                                      dim3((unsigned)blocks), dim3(256), args, 0,
+                                      dim3((unsigned)blocks), dim3(kPerHeadBlock), args, 0,
                                       reinterpret_cast<hipStream_t>(stream)));
 }
 

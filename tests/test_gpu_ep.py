@@ -134,7 +134,9 @@ def test_ep_combine_in_place():
 @pytest.mark.parametrize("G", [1, 2, 8])
 def test_ep_pipeline_on_one_gpu(G):
     """Every rank's partial into one [G, T, H] buffer, then the combine: bit-identical to the
-    oracle's two steps; with one rank, bit-identical to mf_moe_finalize."""
+    oracle's two steps.  With one rank, residual_out is bit-identical to mf_moe_finalize's (the
+    same FMA chain, then one add of +0); out is within one bf16 ulp of it, since the combine's
+    final RMSNorm reduces the mean square over 8 waves and the finalize's over 16."""
     T, H, k = 257, 7168, 8
     d = workloads.make_finalize_inputs(T, H, E=64, k=k, seed=740 + G)
     say(f"ep pipeline T={T} H={H} k={k} G={G}")
@@ -154,7 +156,8 @@ def test_ep_pipeline_on_one_gpu(G):
                                   up(d["residual"]), up(d["gamma"], True), d["eps"])
     torch.cuda.synchronize()
     if G == 1:
-        assert torch.equal(r, r1) and torch.equal(out.view(torch.int16), out1.view(torch.int16))
+        assert torch.equal(r, r1)
+        assert_bf16_close(bits(out), bits(out1))
     else:
         # another grouping of the same sum: within the fp32 rounding of the terms
         x = workloads.bf16_bits_to_f32(d["expert_rows"]).astype(np.float64)[d["idx"]]
