@@ -89,11 +89,19 @@ __device__ __forceinline__ void issue_batch(GatherBatch<VPL, JB, PER_EXPERT, SKI
                                             const FinalizeArgs& a, int64_t tk, int jb, int k,
                                             const Slots<VPL, TAIL>& sl) {
     const int64_t last_row = a.num_rows - 1;
+    // Every index of the batch first (one wide scalar load), then every row load: reading an
+    // index right before its row's load serialises the index loads.
+    int32_t rid[JB], eid[PER_EXPERT ? JB : 1];
+#pragma unroll
+    for (int u = 0; u < JB; ++u) {
+        rid[u] = a.idx[tk + min(jb + u, k - 1)];
+        if constexpr (PER_EXPERT) eid[u] = a.eids[tk + min(jb + u, k - 1)];
+    }
 #pragma unroll
     for (int u = 0; u < JB; ++u) {
         // Past the last j of a partial batch, reload row k-1 (same cache lines; unused).
         const int j = min(jb + u, k - 1);
-        int64_t row = a.idx[tk + j];
+        int64_t row = rid[u];
         if constexpr (SKIP) {
             // another GPU's expert: nothing is read for it (a wave-uniform branch)
             b.live[u] = row >= 0;
@@ -113,7 +121,7 @@ __device__ __forceinline__ void issue_batch(GatherBatch<VPL, JB, PER_EXPERT, SKI
         for (int s = 0; s < VPL; ++s)
             b.x[u][s] = sl.suni[s] ? ld_stream(at<u32x4>(rp, sl.eoff[s] * 2u)) : u32x4{0u, 0u, 0u, 0u};
         if constexpr (PER_EXPERT) {
-            int e = a.eids[tk + j];
+            int e = eid[u];
             e = e < 0 ? 0 : (e >= a.num_experts ? a.num_experts - 1 : e);
             const uint16_t* gp = a.egamma + (int64_t)e * a.H;
 #pragma unroll
@@ -211,12 +219,13 @@ moe_finalize_kernel(const FinalizeArgs a) {
     };
 
     TokenLds L = token_lds(lds, m.wpt, PER_EXPERT ? JB : 1);
+    // The residual and gamma do not depend on the indices: in flight while they arrive.
+    if (!PARTIAL && EARLY) load_res_gamma();
     constexpr int UNROLL = KC > 0 ? (KC + JB - 1) / JB : 1;
 #pragma unroll UNROLL
     for (int jb = 0; jb < k; jb += JB) {
         GatherBatch<VPL, JB, PER_EXPERT, PARTIAL> b;
         issue_batch(b, a, tk, jb, k, sl);
-        if (!PARTIAL && EARLY && jb == 0) load_res_gamma();
         consume_batch(b, acc, a, tk, jb, k, sl, L, m);
     }
     if constexpr (PARTIAL) {
