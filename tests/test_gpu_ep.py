@@ -80,6 +80,7 @@ def per_expert_bound(d, idx):
 @pytest.mark.parametrize("T,H,k,G,pe", [
     (17, 1024, 8, 2, False), (33, 4104, 9, 3, False), (100, 7168, 8, 8, False),
     (5, 32768, 3, 2, False), (64, 4096, 8, 4, True), (9, 520, 5, 2, True), (300, 2048, 1, 4, False),
+    (9, 776, 5, 2, False), (6, 5000, 8, 3, True),
 ])
 def test_ep_partial_matches_oracle(T, H, k, G, pe):
     say(f"ep partial T={T} H={H} k={k} G={G} per_expert={pe}")
@@ -105,7 +106,7 @@ def test_ep_partial_all_remote_is_zero():
 
 
 @pytest.mark.parametrize("T,H,G", [(1, 8, 1), (7, 520, 3), (300, 7168, 8), (5, 32768, 2),
-                                   (2049, 1024, 16), (33, 12288, 5)])
+                                   (2049, 1024, 16), (33, 12288, 5), (7, 776, 3), (4, 20000, 2)])
 def test_ep_combine_matches_oracle(T, H, G):
     say(f"ep combine T={T} H={H} G={G}")
     d = workloads.make_ep_combine_inputs(T, H, G, seed=720 + T + H + G)

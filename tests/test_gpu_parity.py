@@ -115,6 +115,9 @@ FINALIZE_SHAPES = [
     (2049, 7168, 8, "expert_grouped"), (7, 8192, 16, "random"), (5, 12288, 4, "random"),
     (3000, 12288, 2, "expert_grouped"), (4, 32768, 3, "random"), (2100, 32768, 1, "random"),
     (4097, 2048, 5, "expert_grouped"), (6, 3584, 64, "random"),
+    # rows whose last slot ends past its first 256 values (the second 1 KiB residual store is
+    # the partial one)
+    (9, 776, 4, "random"), (65, 5000, 8, "expert_grouped"),
 ]
 
 
@@ -228,7 +231,7 @@ def test_finalize_decode_per_expert_workload():
 
 
 @pytest.mark.parametrize("T,H,k", [(1, 64, 1), (5, 520, 3), (33, 7168, 8), (2100, 7168, 8),
-                                   (3, 4096, 13), (9, 32768, 2), (2500, 1024, 4)])
+                                   (3, 4096, 13), (9, 32768, 2), (2500, 1024, 4), (5, 3848, 8)])
 def test_per_expert_matches_oracle(T, H, k):
     say(f"per-expert T={T} H={H} k={k}: {shape_str(1, T, H, k)}")
     d = workloads.make_finalize_inputs(T, H, E=32, k=k, seed=2000 + T + H + k, per_expert=True,
@@ -271,7 +274,8 @@ def test_gated_workload_full_size():
     assert_bf16_close_given_residual_tol(bits(out), o_ref, r_ref, d["gamma"], d["eps"])
 
 
-@pytest.mark.parametrize("T,H", [(1, 8), (3, 520), (5000, 1024), (7, 32768), (2049, 8192)])
+@pytest.mark.parametrize("T,H", [(1, 8), (3, 520), (5000, 1024), (7, 32768), (2049, 8192),
+                                 (3, 1000)])
 def test_gated_matches_oracle(T, H):
     say(f"gated T={T} H={H}: {shape_str(2, T, H)}")
     d = workloads.make_gated_inputs(T, H, seed=3000 + T + H)
@@ -330,7 +334,7 @@ def test_gated_next_workload_full_size():
 
 
 @pytest.mark.parametrize("T,H", [(1, 8), (3, 520), (5000, 1024), (7, 32768), (2049, 8192),
-                                 (9, 12288)])
+                                 (9, 12288), (5, 7000)])
 def test_gated_next_matches_oracle(T, H):
     say(f"gated next T={T} H={H}: {shape_str(2, T, H)}")
     check_gated_next(workloads.make_gated_inputs(T, H, seed=3100 + T + H, dual=True))
