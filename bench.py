@@ -267,6 +267,8 @@ def launch_config(name: str, d: dict) -> dict:
         return mf.mf_launch_shape(mf.KIND_GATED, d["T"], d["H"])  # the same row shape
     if kind in ("gated", "gated_next"):
         return mf.mf_launch_shape(mf.KIND_GATED, d["T"], d["H"])
+    if kind == "ep_combine":
+        return mf.mf_launch_shape(mf.KIND_EP_COMBINE, d["T"], d["H"])
     return {}
 
 

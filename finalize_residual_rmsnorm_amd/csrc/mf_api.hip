@@ -146,13 +146,17 @@ int mf_moe_finalize_supported(int32_t H, int32_t k, int per_expert) {
 
 int mf_launch_shape(int kind, int64_t T, int32_t H, int32_t k, int32_t* waves_per_token,
                     int32_t* vectors_per_lane, int32_t* block_threads, int64_t* grid_blocks) {
-    if (kind < 0 || kind > 2 || T < 0) return MF_ERR_SHAPE;
+    if (kind < 0 || kind > 3 || T < 0) return MF_ERR_SHAPE;
     if (kind <= 1 ? !mf_moe_finalize_supported(H, k, kind) : !row_width_supported(H))
         return MF_ERR_UNSUPPORTED;
-    const RowShape s = kind <= 1 ? finalize_shape(T, H, k, kind == 1) : row_shape(T, H, kMaxWaves, kMaxVpl);
+    const RowShape s = kind <= 1   ? finalize_shape(T, H, k, kind == 1)
+                       : kind == 2 ? row_shape(T, H, kMaxWaves, kMaxVpl)
+                                   : combine_shape(T, H);
     if (T > 0 && !grid_fits(s.grid, s.block)) return MF_ERR_SHAPE;
     // the same kernel lookup as the launch itself
-    const void* fn = kind <= 1 ? finalize_kernel_for(s, k, kind == 1) : gated_kernel_for(s, false);
+    const void* fn = kind <= 1   ? finalize_kernel_for(s, k, kind == 1)
+                     : kind == 2 ? gated_kernel_for(s, false)
+                                 : combine_kernel_for(s);
     if (!fn || (kind <= 1 && s.block > finalize_block_max(kind == 1))) return MF_ERR_UNSUPPORTED;
     if (waves_per_token) *waves_per_token = s.wpt;
     if (vectors_per_lane) *vectors_per_lane = s.vpl;

@@ -257,6 +257,12 @@ def test_launch_shapes():
         waves_per_token=8, vectors_per_lane=3, block=512, grid=5)
     # the widest row: 64 slots over 16 waves
     assert mf.mf_launch_shape(mf.KIND_FINALIZE, 100000, 32768, 8)["vectors_per_lane"] == 4
+    # the EP combine runs at most 8 waves per token, 16 when 8 waves of 4 slots cannot hold the row
+    assert mf.mf_launch_shape(mf.KIND_EP_COMBINE, 2048, 7168) == dict(
+        waves_per_token=8, vectors_per_lane=2, block=512, grid=2048)
+    assert mf.mf_launch_shape(mf.KIND_EP_COMBINE, 4, 16384)["waves_per_token"] == 8
+    assert mf.mf_launch_shape(mf.KIND_EP_COMBINE, 4, 20000) == dict(
+        waves_per_token=16, vectors_per_lane=3, block=1024, grid=4)
     with pytest.raises(mf.MFError):
         mf.mf_launch_shape(mf.KIND_FINALIZE, 4, 1001, 2)
 
@@ -267,7 +273,7 @@ def test_every_supported_width_has_a_kernel():
     for H in range(8, 32768 + 1, 8):
         for kind, k in ((mf.KIND_FINALIZE, 8), (mf.KIND_FINALIZE, 3),
                         (mf.KIND_FINALIZE_PER_EXPERT, 8), (mf.KIND_FINALIZE_PER_EXPERT, 5),
-                        (mf.KIND_GATED, 1)):
+                        (mf.KIND_GATED, 1), (mf.KIND_EP_COMBINE, 1)):
             s = mf.mf_launch_shape(kind, 1000, H, k)
             assert s["waves_per_token"] * s["vectors_per_lane"] * 512 >= H, (kind, H, k)
             assert s["block"] <= (512 if kind == mf.KIND_FINALIZE_PER_EXPERT else 1024)
