@@ -1,5 +1,5 @@
 // Host side of the routing entry points declared in include/mf.h: argument checks (before any
-// HIP call), the launch plan and the three launches.  Stateless and allocation-free: the
+// HIP call), the launch plan and the launches (two for small calls, three otherwise).  Stateless and allocation-free: the
 // caller passes the workspace.
 #include <hip/hip_runtime.h>
 
@@ -121,6 +121,11 @@ int mf_moe_route(const float* logits, int64_t T, int32_t num_experts, int32_t k,
                                              dim3(kRouteWaves * kWave), args,
                                              route_select_lds_bytes(E), s);
         if (e != hipSuccess) return MF_ERR_HIP;
+    }
+    if (p.nblocks * E <= kRouteFinishCells && T * k <= kRouteFinishSlots) {
+        // small calls: the scan and the scatter in one workgroup
+        return hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&route_finish_kernel),
+                                          dim3(1), dim3(kRouteScatterThreads), args, 0, s));
     }
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&route_scan_kernel),
                                    dim3(unsigned((E + kWave - 1) / kWave)),

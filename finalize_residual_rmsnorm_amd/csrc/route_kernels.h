@@ -34,6 +34,8 @@
 //  3. route_scatter_kernel: one thread per expert: offsets = exclusive scan of the totals over
 //     the experts, and a per-block LDS table offsets[e] + block prefix[e]; then for every slot
 //     p = table[e] + rank: idx[s] = p, perm[p] = s.
+// Small calls (decode sizes) replace kernels 2 and 3 by route_finish_kernel, one workgroup that
+// does both: two launches instead of three.
 // Everything but the weights is integer work, exact and independent of the launch shape.
 #pragma once
 
@@ -252,6 +254,21 @@ __device__ __forceinline__ void select_strided(const float (&x)[EPL], int lane, 
     top = from_ordered_bits(top_o);
 }
 
+// One token's top-k and softmax over its logits x (laid out for EPL): lane j < k receives the
+// j-th expert and its weight exp(l_j - l_0) / sum_i exp(l_i - l_0) (fp32, the sum in j order).
+template <int EPL>
+__device__ __forceinline__ void route_token(const float (&x)[EPL], int lane, int E, int k,
+                                            int& my_e, float& w) {
+    float my_v = 0.0f, top = 0.0f;
+    my_e = 0;
+    if constexpr (EPL <= kSortedMaxEpl) select_sorted<EPL>(x, lane, E, k, my_e, my_v, top);
+    else select_strided<EPL>(x, lane, E, k, my_e, my_v, top);
+    const float ex = expf(my_v - top);
+    float sum = 0.0f;
+    for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+    w = ex / sum;
+}
+
 // EPL: logits per lane, E <= 64 * EPL.  VEC: vector loads of the logits (see load_logits).
 template <int EPL, bool VEC>
 __global__ void __launch_bounds__(kRouteWaves * kWave) route_select_kernel(const RouteArgs a) {
@@ -275,16 +292,12 @@ __global__ void __launch_bounds__(kRouteWaves * kWave) route_select_kernel(const
         const int64_t t = tw0 + i;
         // the next token's logits (the last token re-reads its own row: no branch, in bounds)
         load_logits<EPL, kLaneMajor, VEC>(xn, a.logits + (i + 1 < ntok ? t + 1 : t) * E, E, lane);
-        int my_e = 0;
-        float my_v = 0.0f, top = 0.0f;
-        if constexpr (kLaneMajor) select_sorted<EPL>(x, lane, E, k, my_e, my_v, top);
-        else select_strided<EPL>(x, lane, E, k, my_e, my_v, top);
-        const float ex = expf(my_v - top);
-        float sum = 0.0f;
-        for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+        int my_e;
+        float w;
+        route_token<EPL>(x, lane, E, k, my_e, w);
         if (lane < k) {
             a.expert_ids[t * k + lane] = my_e;
-            a.weights[t * k + lane] = ex / sum;
+            a.weights[t * k + lane] = w;
             stage[i * k + lane] = uint16_t(my_e);
         }
 #pragma unroll
@@ -455,6 +468,60 @@ __global__ void __launch_bounds__(kRouteScatterThreads) route_scatter_kernel(con
         if (p < 0 || p >= total) continue;  // never taken: the ranks of an expert are distinct
         a.idx[s] = int32_t(p);
         a.perm[p] = int32_t(s);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Small calls (a per-block count table of at most kRouteFinishCells entries and at most
+// kRouteFinishSlots slots, e.g. decode): kernels 2 and 3 in one workgroup of 1024 threads,
+// which saves a launch (about the floor of a small kernel).  Same results as kernels 2 and 3.
+//  1. one thread per expert: the exclusive prefix of its block counts over the blocks (in
+//     LDS) and its total;
+//  2. offsets = exclusive scan of the totals over the experts, added to every block prefix;
+//  3. every slot s of block b: p = offsets[e] + prefix[b][e] + (its rank within the block,
+//     left in idx by kernel 1); idx[s] = p, perm[p] = s.
+constexpr int kRouteFinishCells = 8192;
+constexpr int kRouteFinishSlots = 16384;
+static_assert(kRouteScatterThreads == kRouteMaxE, "one thread per expert in the finish kernel");
+
+__global__ void __launch_bounds__(kRouteScatterThreads) route_finish_kernel(const RouteArgs a) {
+    __shared__ int32_t pre[kRouteFinishCells];  // [nblocks][E]
+    __shared__ int32_t wtot[kRouteScatterThreads / kWave];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int E = a.E, k = a.k, nb = a.nblocks;
+    const int e = tid;
+    int run = 0;
+    if (e < E) {
+        for (int b = 0; b < nb; ++b) {
+            const int c = a.counts[int64_t(b) * E + e];
+            pre[b * E + e] = run;
+            run += c;
+        }
+    }
+    const int incl = wave_inclusive_scan(run, lane);
+    if (lane == kWave - 1) wtot[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wtot[w];
+    const int off = before + incl - run;  // slots routed to experts below e
+    if (e < E) {
+        a.offsets[e] = off;
+        if (e == E - 1) a.offsets[E] = off + run;  // the total T*k
+        for (int b = 0; b < nb; ++b) pre[b * E + e] += off;
+    }
+    __syncthreads();
+    const int total = int(a.T) * k;
+    const int per = kRouteWaves * a.tpw * k;  // slots per block of kernel 1
+    for (int s = tid; s < total; s += kRouteScatterThreads) {
+        const int ex = a.expert_ids[s];
+        const int b = s / per;
+        if (ex < 0 || ex >= E || b >= nb) continue;  // never taken: ids are below E
+        const int p = pre[b * E + ex] + a.idx[s];
+        if (p < 0 || p >= total) continue;  // never taken: the ranks of an expert are distinct
+        a.idx[s] = p;
+        a.perm[p] = s;
     }
 }
 

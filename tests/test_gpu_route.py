@@ -88,13 +88,18 @@ def test_route_named_workloads(name):
 
 
 ROUTE_SHAPES = [
-    # (T, E, k, bf16-valued logits): one expert; every logits-per-lane instantiation
+    # (T, E, k, bf16-valued logits): one expert; every logits-per-lane instantiation, on the
+    # two-launch path of small calls and the three-launch path
     # (E <= 64, 128, 256, 512, 1024); k from 1 to 16 and k == E; ragged T around the
     # 16-wave blocks and the 64-slot chunks; T large enough for 16 tokens per wave.
     (1, 1, 1, False), (3, 8, 2, False), (37, 8, 8, True), (64, 130, 16, False),
     (300, 64, 1, True), (1000, 256, 8, True), (4097, 16, 4, False), (9000, 5, 3, True),
     (40, 1024, 16, False), (8200, 33, 2, True), (5, 513, 16, False), (2, 65, 1, False),
     (17, 16, 16, True), (100000, 256, 8, False), (70001, 1024, 16, True), (65537, 64, 6, True),
+    # either side of the two-launch path's limits (a per-block count table of at most 8192
+    # entries: 16 tokens per block below T = 4096; at most 16384 slots)
+    (512, 256, 8, False), (600, 256, 8, False), (128, 1024, 16, True), (129, 1024, 16, True),
+    (2048, 32, 1, True), (4096, 16, 4, False),
 ]
 
 
