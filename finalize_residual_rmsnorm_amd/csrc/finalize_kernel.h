@@ -15,8 +15,9 @@
 //    residual is read once and written once and nothing is re-read.
 //  - Gathers are 16-byte loads, a full contiguous 1 KiB per wave instruction.  A batch of
 //    rows is issued in full before any of it is used; with the compile-time top-k (k = 8)
-//    the token's indices and weights come in a few wide scalar loads and all k rows, the
-//    residual and gamma are in flight at once, so a token costs about one memory round trip.
+//    the token's indices and weights come in a few wide scalar loads, and the residual, gamma
+//    and all k rows are then in flight at once, so a token costs the index loads and about
+//    one more memory round trip.
 //  - No MFMA: the arithmetic intensity is below 1 flop per byte; the kernel is bound by HBM.
 //  - No atomics and a fixed reduction order: results are bit-deterministic and identical for
 //    a token whatever batch it is in.
@@ -91,6 +92,7 @@ __device__ __forceinline__ void issue_batch(GatherBatch<VPL, JB, PER_EXPERT, SKI
     const int64_t last_row = a.num_rows - 1;
     // Every index of the batch first (one wide scalar load), then every row load: reading an
     // index right before its row's load serialises the index loads.
+    // Past the last j of a partial batch, row k-1 is loaded again (same cache lines; unused).
     int32_t rid[JB], eid[PER_EXPERT ? JB : 1];
 #pragma unroll
     for (int u = 0; u < JB; ++u) {
@@ -99,8 +101,6 @@ __device__ __forceinline__ void issue_batch(GatherBatch<VPL, JB, PER_EXPERT, SKI
     }
 #pragma unroll
     for (int u = 0; u < JB; ++u) {
-        // Past the last j of a partial batch, reload row k-1 (same cache lines; unused).
-        const int j = min(jb + u, k - 1);
         int64_t row = rid[u];
         if constexpr (SKIP) {
             // another GPU's expert: nothing is read for it (a wave-uniform branch)

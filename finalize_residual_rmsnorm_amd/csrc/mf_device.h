@@ -36,8 +36,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// Address `base + byte_off` with a 32-bit unsigned offset: with a wave-uniform base this is
-// the SGPR-base + VGPR-offset form of global loads/stores (no 64-bit address per lane).
+// Address `base + byte_off` with a 32-bit unsigned offset: with a wave-uniform base this allows
+// the SGPR-base + VGPR-offset form of global loads/stores (no 64-bit address per lane; the
+// compiler may still form per-lane addresses, e.g. when it shares `base + offset` between
+// several uniform bases).
 template <class T>
 __device__ __forceinline__ const T* at(const void* base, uint32_t byte_off) {
     return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
@@ -52,6 +54,7 @@ template <class T>
 __device__ __forceinline__ T ld_stream(const T* p) { return __builtin_nontemporal_load(p); }
 template <class T>
 __device__ __forceinline__ void st_stream(T v, T* p) { __builtin_nontemporal_store(v, p); }
+
 // A load whose cache policy is a compile-time choice (nontemporal or default).
 template <bool NT, class T>
 __device__ __forceinline__ T ld_policy(const T* p) {

@@ -144,8 +144,10 @@ __device__ __forceinline__ float lane_sumsq(const float (&r)[VPL][8], const Slot
 // ds_bpermute: for the first store lane l takes slot elements 4l..4l+3 (the first or second
 // half of lane l/2's values), for the second 256+4l..256+4l+3 (from lane 32 + l/2), and each
 // store instruction writes 1 KiB contiguous.  A store is valid exactly when its source lane's
-// values are, since H % 8 == 0.  Measured: the finalize 1.5% and the gated-residual norm 7%
-// faster than the direct stores, results identical.
+// values are, since H % 8 == 0.  Every lane of the wave must be active.  Used for every fp32
+// row the kernels write (the residual, the expert-parallel partial).  Measured: the finalize
+// 1.5% and the gated-residual norm 7% faster than the direct stores, results identical.
+// (The slots argument only selects the tail handling.)
 template <int VPL, int TAIL>
 __device__ __forceinline__ void store_residual(const float (&r)[VPL][8], const Slots<VPL, TAIL>&,
                                                const RowMap& m, int H, float* row) {
