@@ -118,6 +118,8 @@ FINALIZE_SHAPES = [
     # rows whose last slot ends past its first 256 values (the second 1 KiB residual store is
     # the partial one)
     (9, 776, 4, "random"), (65, 5000, 8, "expert_grouped"),
+    # a grid past 65535 workgroups
+    (70000, 64, 2, "random"),
 ]
 
 
@@ -275,7 +277,7 @@ def test_gated_workload_full_size():
 
 
 @pytest.mark.parametrize("T,H", [(1, 8), (3, 520), (5000, 1024), (7, 32768), (2049, 8192),
-                                 (3, 1000)])
+                                 (3, 1000), (70000, 72)])
 def test_gated_matches_oracle(T, H):
     say(f"gated T={T} H={H}: {shape_str(2, T, H)}")
     d = workloads.make_gated_inputs(T, H, seed=3000 + T + H)
