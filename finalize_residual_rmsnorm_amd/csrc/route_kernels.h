@@ -68,10 +68,12 @@ constexpr int kRouteChunks = kRouteSlotsPerWave / kWave;
 constexpr int kRouteScatterThreads = kRouteMaxE;  // one thread per expert
 constexpr int kRouteScatterSlots = kRouteWaves * kRouteSlotsPerWave / kRouteScatterThreads;
 
-// LDS of kernel 1: per-wave per-expert counts and the wave's expert ids in slot order (both
-// 16-bit: a wave holds at most 256 slots and a block 4096).
+// LDS of kernel 1: the wave's weights in slot order (fp32), then per-wave per-expert counts and
+// the wave's expert ids in slot order (both 16-bit: a wave holds at most 256 slots and a block
+// 4096).
 constexpr size_t route_select_lds_bytes(int E) {
-    return size_t(kRouteWaves) * (E + kRouteSlotsPerWave) * sizeof(uint16_t);
+    return size_t(kRouteWaves) * kRouteSlotsPerWave * sizeof(float) +
+           size_t(kRouteWaves) * (E + kRouteSlotsPerWave) * sizeof(uint16_t);
 }
 
 // Orders the program-order LDS accesses of one wave's lanes (no hardware wait needed:
@@ -272,10 +274,12 @@ __device__ __forceinline__ void route_token(const float (&x)[EPL], int lane, int
 // EPL: logits per lane, E <= 64 * EPL.  VEC: vector loads of the logits (see load_logits).
 template <int EPL, bool VEC>
 __global__ void __launch_bounds__(kRouteWaves * kWave) route_select_kernel(const RouteArgs a) {
-    extern __shared__ uint16_t route_lds[];
+    extern __shared__ float route_lds_f[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int E = a.E, k = a.k;
+    float* wstage = route_lds_f + wave * kRouteSlotsPerWave;       // [kRouteWaves][256] weights
+    uint16_t* route_lds = reinterpret_cast<uint16_t*>(route_lds_f + kRouteWaves * kRouteSlotsPerWave);
     uint16_t* cnt = route_lds;                                     // [kRouteWaves][E]
     uint16_t* mycnt = cnt + wave * E;
     uint16_t* stage = route_lds + kRouteWaves * E + wave * kRouteSlotsPerWave;
@@ -285,6 +289,9 @@ __global__ void __launch_bounds__(kRouteWaves * kWave) route_select_kernel(const
     for (int e = lane; e < E; e += kWave) mycnt[e] = 0;
 
     // --- top-k and softmax, one token at a time; the next token's logits are in flight ---
+    // The results are staged in LDS and stored at the end of the kernel: a global store inside
+    // the loop (under lane < k) made every iteration's wait for the next logits also wait for
+    // the previous token's stores to complete (loads and stores share one counter on gfx950).
     constexpr bool kLaneMajor = EPL <= kSortedMaxEpl;
     float x[EPL], xn[EPL];
     if (ntok > 0) load_logits<EPL, kLaneMajor, VEC>(x, a.logits + tw0 * E, E, lane);
@@ -296,8 +303,7 @@ __global__ void __launch_bounds__(kRouteWaves * kWave) route_select_kernel(const
         float w;
         route_token<EPL>(x, lane, E, k, my_e, w);
         if (lane < k) {
-            a.expert_ids[t * k + lane] = my_e;
-            a.weights[t * k + lane] = w;
+            wstage[i * k + lane] = w;
             stage[i * k + lane] = uint16_t(my_e);
         }
 #pragma unroll
@@ -308,14 +314,17 @@ __global__ void __launch_bounds__(kRouteWaves * kWave) route_select_kernel(const
     // --- rank of each slot among the wave's earlier slots of the same expert ---
     const int ns = ntok * k;
     int rank[kRouteChunks], ce[kRouteChunks];
+    float cw[kRouteChunks];
 #pragma unroll
     for (int c = 0; c < kRouteChunks; ++c) {
         rank[c] = 0;
         ce[c] = 0;
+        cw[c] = 0.0f;
         if (c * kWave < ns) {
             const int sl = c * kWave + lane;
             const bool valid = sl < ns;
             const int e = valid ? stage[sl] : 0;
+            cw[c] = valid ? wstage[sl] : 0.0f;
             // m: the chunk's lanes whose expert has every id bit equal to this lane's
             uint64_t m = __builtin_amdgcn_ballot_w64(valid);
             for (int b = 0; b < a.id_bits; ++b) {
@@ -348,10 +357,16 @@ __global__ void __launch_bounds__(kRouteWaves * kWave) route_select_kernel(const
         a.counts[int64_t(blockIdx.x) * E + e] = run;
     }
     __syncthreads();
+    // Every global store of the wave's slots comes last: a store before a barrier or a wave
+    // fence would be waited for there.  A wave's slots are contiguous, so these are coalesced.
 #pragma unroll
     for (int c = 0; c < kRouteChunks; ++c) {
         const int sl = c * kWave + lane;
-        if (sl < ns) a.idx[tw0 * k + sl] = rank[c] + mycnt[ce[c]];
+        if (sl < ns) {
+            a.expert_ids[tw0 * k + sl] = ce[c];
+            a.weights[tw0 * k + sl] = cw[c];
+            a.idx[tw0 * k + sl] = rank[c] + mycnt[ce[c]];
+        }
     }
 }
 
