@@ -106,7 +106,12 @@ def test_ep_partial_all_remote_is_zero():
 
 
 @pytest.mark.parametrize("T,H,G", [(1, 8, 1), (7, 520, 3), (300, 7168, 8), (5, 32768, 2),
-                                   (2049, 1024, 16), (33, 12288, 5), (7, 776, 3), (4, 20000, 2)])
+                                   (2049, 1024, 16), (33, 12288, 5), (7, 776, 3), (4, 20000, 2),
+                                   # two slots per wave, two ranks in flight: an odd rank count
+                                   # and a single rank end the rotation part-way
+                                   (65, 7168, 5), (3, 7168, 1), (10, 6000, 7),
+                                   # a live wave whose second slot lies past the row
+                                   (9, 6656, 3)])
 def test_ep_combine_matches_oracle(T, H, G):
     say(f"ep combine T={T} H={H} G={G}")
     d = workloads.make_ep_combine_inputs(T, H, G, seed=720 + T + H + G)
