@@ -27,8 +27,8 @@
 //     expert comes from ballots over the bits of the expert id (the ballot / prefix-count
 //     technique of the PR #4130 page's warp-cooperative scheduler, "why is this good" item 2),
 //     added to the wave's running per-expert count in LDS.  The waves' counts are scanned in
-//     wave order; idx receives each slot's rank within its block, the workspace the block's
-//     per-expert counts.
+//     wave order; the workspace receives the block's per-expert counts, and at the very end
+//     expert_ids, weights and idx (each slot's rank within its block) are stored, coalesced.
 //  2. route_scan_kernel: per expert, the exclusive scan of the block counts over the blocks
 //     (in place) and the expert's total.
 //  3. route_scatter_kernel: one thread per expert: offsets = exclusive scan of the totals over
