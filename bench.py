@@ -275,7 +275,7 @@ def launch_config(name: str, d: dict) -> dict:
 # ------------------------------------------------------------------------------ CPU oracle
 
 
-def cpu_baseline(d: dict, target_cpu_s: float = 15.0, max_threads: int = 16) -> dict:
+def cpu_baseline(d: dict, target_cpu_s: float = 20.0, max_threads: int = 16) -> dict:
     """The CPU oracle on a bounded sample (about target_cpu_s of CPU work) of the workload's
     tokens, split over up to max_threads host threads (the call releases the GIL)."""
     from concurrent.futures import ThreadPoolExecutor
