@@ -11,8 +11,10 @@ bf16 tensors are torch.bfloat16; fp32 tensors torch.float32; indices torch.int32
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
+import threading
 
 import torch
 
@@ -91,11 +93,32 @@ def _check(fn: str, status: int) -> None:
         raise MFError(fn, status)
 
 
+_call = threading.local()
+
+
+@contextlib.contextmanager
+def _on(device: torch.device):
+    """Run one library call with `device` current (the library launches on the current HIP
+    device) and require every tensor passed through _dev inside it to live there."""
+    if device.type != "cuda":
+        raise ValueError(f"expected GPU tensors, got device {device}")
+    prev = getattr(_call, "device", None)
+    _call.device = device
+    try:
+        with torch.cuda.device(device):
+            yield
+    finally:
+        _call.device = prev
+
+
 def _dev(t: torch.Tensor, dtype: torch.dtype, name: str, shape=None) -> int:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name}: expected a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name}: must be a GPU tensor, got device {t.device}")
+    want = getattr(_call, "device", None)
+    if want is not None and t.device != want:
+        raise ValueError(f"{name}: on {t.device}, but the call's other tensors are on {want}")
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
     if not t.is_contiguous():
@@ -138,13 +161,15 @@ def mf_moe_finalize(expert_rows: torch.Tensor, idx: torch.Tensor, weights: torch
         E = expert_gamma.shape[0]
         pe = _dev(expert_ids, torch.int32, "expert_ids", (T, k))
         pg = _dev(expert_gamma, torch.bfloat16, "expert_gamma", (E, H))
-    st = lib().mf_moe_finalize(
-        _dev(expert_rows, torch.bfloat16, "expert_rows"), num_rows,
-        _dev(idx, torch.int32, "idx"), _dev(weights, torch.float32, "weights", (T, k)), pe, pg, E,
-        _dev(residual, torch.float32, "residual", (T, H)),
-        _dev(residual_out, torch.float32, "residual_out", (T, H)),
-        _dev(gamma, torch.bfloat16, "gamma", (H,)), float(eps),
-        _dev(out, torch.bfloat16, "out", (T, H)), T, H, k, _stream(stream, dev))
+    with _on(dev):
+        st = lib().mf_moe_finalize(
+            _dev(expert_rows, torch.bfloat16, "expert_rows"), num_rows,
+            _dev(idx, torch.int32, "idx"), _dev(weights, torch.float32, "weights", (T, k)),
+            pe, pg, E,
+            _dev(residual, torch.float32, "residual", (T, H)),
+            _dev(residual_out, torch.float32, "residual_out", (T, H)),
+            _dev(gamma, torch.bfloat16, "gamma", (H,)), float(eps),
+            _dev(out, torch.bfloat16, "out", (T, H)), T, H, k, _stream(stream, dev))
     _check("mf_moe_finalize", st)
     return out, residual_out
 
@@ -169,10 +194,12 @@ def mf_moe_finalize_ep_partial(expert_rows: torch.Tensor, idx: torch.Tensor,
         E = expert_gamma.shape[0]
         pe = _dev(expert_ids, torch.int32, "expert_ids", (T, k))
         pg = _dev(expert_gamma, torch.bfloat16, "expert_gamma", (E, H))
-    st = lib().mf_moe_finalize_ep_partial(
-        _dev(expert_rows, torch.bfloat16, "expert_rows"), num_rows, _dev(idx, torch.int32, "idx"),
-        _dev(weights, torch.float32, "weights", (T, k)), pe, pg, E, float(eps),
-        _dev(partial, torch.float32, "partial", (T, H)), T, H, k, _stream(stream, dev))
+    with _on(dev):
+        st = lib().mf_moe_finalize_ep_partial(
+            _dev(expert_rows, torch.bfloat16, "expert_rows"), num_rows,
+            _dev(idx, torch.int32, "idx"),
+            _dev(weights, torch.float32, "weights", (T, k)), pe, pg, E, float(eps),
+            _dev(partial, torch.float32, "partial", (T, H)), T, H, k, _stream(stream, dev))
     _check("mf_moe_finalize_ep_partial", st)
     return partial
 
@@ -188,12 +215,13 @@ def mf_moe_finalize_ep_combine(partials: torch.Tensor, residual: torch.Tensor, g
         residual_out = torch.empty((T, H), dtype=torch.float32, device=dev)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    st = lib().mf_moe_finalize_ep_combine(
-        _dev(partials, torch.float32, "partials"), G,
-        _dev(residual, torch.float32, "residual", (T, H)),
-        _dev(residual_out, torch.float32, "residual_out", (T, H)),
-        _dev(gamma, torch.bfloat16, "gamma", (H,)), float(eps),
-        _dev(out, torch.bfloat16, "out", (T, H)), T, H, _stream(stream, dev))
+    with _on(dev):
+        st = lib().mf_moe_finalize_ep_combine(
+            _dev(partials, torch.float32, "partials"), G,
+            _dev(residual, torch.float32, "residual", (T, H)),
+            _dev(residual_out, torch.float32, "residual_out", (T, H)),
+            _dev(gamma, torch.bfloat16, "gamma", (H,)), float(eps),
+            _dev(out, torch.bfloat16, "out", (T, H)), T, H, _stream(stream, dev))
     _check("mf_moe_finalize_ep_combine", st)
     return out, residual_out
 
@@ -209,12 +237,13 @@ def mf_gated_residual_rmsnorm(x: torch.Tensor, gate: torch.Tensor, residual: tor
         residual_out = torch.empty((T, H), dtype=torch.float32, device=dev)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    st = lib().mf_gated_residual_rmsnorm(
-        _dev(x, torch.bfloat16, "x"), _dev(gate, torch.bfloat16, "gate", (T, H)),
-        _dev(residual, torch.float32, "residual", (T, H)),
-        _dev(residual_out, torch.float32, "residual_out", (T, H)),
-        _dev(gamma, torch.bfloat16, "gamma", (H,)), float(eps),
-        _dev(out, torch.bfloat16, "out", (T, H)), T, H, _stream(stream, dev))
+    with _on(dev):
+        st = lib().mf_gated_residual_rmsnorm(
+            _dev(x, torch.bfloat16, "x"), _dev(gate, torch.bfloat16, "gate", (T, H)),
+            _dev(residual, torch.float32, "residual", (T, H)),
+            _dev(residual_out, torch.float32, "residual_out", (T, H)),
+            _dev(gamma, torch.bfloat16, "gamma", (H,)), float(eps),
+            _dev(out, torch.bfloat16, "out", (T, H)), T, H, _stream(stream, dev))
     _check("mf_gated_residual_rmsnorm", st)
     return out, residual_out
 
@@ -234,14 +263,16 @@ def mf_gated_residual_next_rmsnorm(x: torch.Tensor, gate: torch.Tensor, residual
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     if out_next is None:
         out_next = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    st = lib().mf_gated_residual_next_rmsnorm(
-        _dev(x, torch.bfloat16, "x"), _dev(gate, torch.bfloat16, "gate", (T, H)),
-        _dev(residual, torch.float32, "residual", (T, H)),
-        _dev(residual_out, torch.float32, "residual_out", (T, H)),
-        _dev(gamma, torch.bfloat16, "gamma", (H,)),
-        _dev(gamma_next, torch.bfloat16, "gamma_next", (H,)), float(eps),
-        _dev(out, torch.bfloat16, "out", (T, H)), _dev(out_next, torch.bfloat16, "out_next", (T, H)),
-        T, H, _stream(stream, dev))
+    with _on(dev):
+        st = lib().mf_gated_residual_next_rmsnorm(
+            _dev(x, torch.bfloat16, "x"), _dev(gate, torch.bfloat16, "gate", (T, H)),
+            _dev(residual, torch.float32, "residual", (T, H)),
+            _dev(residual_out, torch.float32, "residual_out", (T, H)),
+            _dev(gamma, torch.bfloat16, "gamma", (H,)),
+            _dev(gamma_next, torch.bfloat16, "gamma_next", (H,)), float(eps),
+            _dev(out, torch.bfloat16, "out", (T, H)),
+            _dev(out_next, torch.bfloat16, "out_next", (T, H)),
+            T, H, _stream(stream, dev))
     _check("mf_gated_residual_next_rmsnorm", st)
     return out, out_next, residual_out
 
@@ -253,10 +284,11 @@ def mf_rmsnorm_sigmoid_gate(x: torch.Tensor, gate: torch.Tensor, gamma: torch.Te
     dev = x.device
     if out is None:
         out = torch.empty_like(x)
-    st = lib().mf_rmsnorm_sigmoid_gate(
-        _dev(x, torch.bfloat16, "x"), _dev(gate, torch.bfloat16, "gate", (T, heads, D)),
-        _dev(gamma, torch.bfloat16, "gamma", (D,)), float(eps),
-        _dev(out, torch.bfloat16, "out", (T, heads, D)), T, heads, D, _stream(stream, dev))
+    with _on(dev):
+        st = lib().mf_rmsnorm_sigmoid_gate(
+            _dev(x, torch.bfloat16, "x"), _dev(gate, torch.bfloat16, "gate", (T, heads, D)),
+            _dev(gamma, torch.bfloat16, "gamma", (D,)), float(eps),
+            _dev(out, torch.bfloat16, "out", (T, heads, D)), T, heads, D, _stream(stream, dev))
     _check("mf_rmsnorm_sigmoid_gate", st)
     return out
 
@@ -295,13 +327,16 @@ def mf_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     """Copy src into dst (same byte size, a multiple of 16) with the library's copy kernel."""
     if src.device.type != "cuda" or dst.device.type != "cuda":
         raise ValueError("mf_stream_copy: GPU tensors required")
+    if src.device != dst.device:
+        raise ValueError("mf_stream_copy: src and dst on different devices")
     if not (src.is_contiguous() and dst.is_contiguous()):
         raise ValueError("mf_stream_copy: contiguous tensors required")
     n = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != n:
         raise ValueError("mf_stream_copy: size mismatch")
-    _check("mf_stream_copy", lib().mf_stream_copy(src.data_ptr(), dst.data_ptr(), n,
-                                                  _stream(stream, src.device)))
+    with _on(src.device):
+        _check("mf_stream_copy", lib().mf_stream_copy(src.data_ptr(), dst.data_ptr(), n,
+                                                      _stream(stream, src.device)))
 
 
 def mf_moe_route_supported(num_experts: int, k: int) -> bool:
@@ -338,12 +373,14 @@ def mf_moe_route(logits: torch.Tensor, k: int, *, expert_ids: torch.Tensor | Non
     workspace = new((ws_bytes,), torch.uint8) if workspace is None else workspace
     if workspace.dtype != torch.uint8 or workspace.dim() != 1:
         raise TypeError("workspace: expected a 1-d torch.uint8 tensor")
-    st = lib().mf_moe_route(
-        _dev(logits, torch.float32, "logits"), T, E, k,
-        _dev(expert_ids, torch.int32, "expert_ids", (T, k)),
-        _dev(weights, torch.float32, "weights", (T, k)), _dev(idx, torch.int32, "idx", (T, k)),
-        _dev(perm, torch.int32, "perm", (T * k,)), _dev(offsets, torch.int32, "offsets", (E + 1,)),
-        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream, dev))
+    with _on(dev):
+        st = lib().mf_moe_route(
+            _dev(logits, torch.float32, "logits"), T, E, k,
+            _dev(expert_ids, torch.int32, "expert_ids", (T, k)),
+            _dev(weights, torch.float32, "weights", (T, k)), _dev(idx, torch.int32, "idx", (T, k)),
+            _dev(perm, torch.int32, "perm", (T * k,)),
+            _dev(offsets, torch.int32, "offsets", (E + 1,)),
+            _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream, dev))
     _check("mf_moe_route", st)
     return expert_ids, weights, idx, perm, offsets
 
@@ -366,10 +403,11 @@ def mf_mxfp4_quantize(x: torch.Tensor, *, q: torch.Tensor | None = None,
     byte, even value in the low nibble; scales uint8 [T, H/32]: E8M0 codes)."""
     T, H = x.shape
     q, scales = _mx_outputs(T, H, x.device, q, scales)
-    st = lib().mf_mxfp4_quantize(_dev(x, torch.float32, "x"), T, H,
-                                 _dev(q, torch.uint8, "q", (T, H // 2)),
-                                 _dev(scales, torch.uint8, "scales", (T, H // 32)),
-                                 _stream(stream, x.device))
+    with _on(x.device):
+        st = lib().mf_mxfp4_quantize(_dev(x, torch.float32, "x"), T, H,
+                                     _dev(q, torch.uint8, "q", (T, H // 2)),
+                                     _dev(scales, torch.uint8, "scales", (T, H // 32)),
+                                     _stream(stream, x.device))
     _check("mf_mxfp4_quantize", st)
     return q, scales
 
@@ -380,11 +418,13 @@ def mf_rmsnorm_mxfp4_quantize(x: torch.Tensor, gamma: torch.Tensor, eps: float =
     """RMSNorm of bf16 rows x [T, H] with gamma, then MXFP4.  Returns (q, scales) as above."""
     T, H = x.shape
     q, scales = _mx_outputs(T, H, x.device, q, scales)
-    st = lib().mf_rmsnorm_mxfp4_quantize(_dev(x, torch.bfloat16, "x"),
-                                         _dev(gamma, torch.bfloat16, "gamma", (H,)), float(eps),
-                                         _dev(q, torch.uint8, "q", (T, H // 2)),
-                                         _dev(scales, torch.uint8, "scales", (T, H // 32)), T, H,
-                                         _stream(stream, x.device))
+    with _on(x.device):
+        st = lib().mf_rmsnorm_mxfp4_quantize(_dev(x, torch.bfloat16, "x"),
+                                             _dev(gamma, torch.bfloat16, "gamma", (H,)), float(eps),
+                                             _dev(q, torch.uint8, "q", (T, H // 2)),
+                                             _dev(scales, torch.uint8, "scales", (T, H // 32)),
+                                             T, H,
+                                             _stream(stream, x.device))
     _check("mf_rmsnorm_mxfp4_quantize", st)
     return q, scales
 
@@ -401,13 +441,16 @@ def mf_moe_finalize_mxfp4(expert_rows: torch.Tensor, idx: torch.Tensor, weights:
     if residual_out is None:
         residual_out = torch.empty((T, H), dtype=torch.float32, device=dev)
     q, scales = _mx_outputs(T, H, dev, q, scales)
-    st = lib().mf_moe_finalize_mxfp4(
-        _dev(expert_rows, torch.bfloat16, "expert_rows"), num_rows, _dev(idx, torch.int32, "idx"),
-        _dev(weights, torch.float32, "weights", (T, k)),
-        _dev(residual, torch.float32, "residual", (T, H)),
-        _dev(residual_out, torch.float32, "residual_out", (T, H)),
-        _dev(gamma, torch.bfloat16, "gamma", (H,)), float(eps),
-        _dev(q, torch.uint8, "q", (T, H // 2)), _dev(scales, torch.uint8, "scales", (T, H // 32)),
-        T, H, k, _stream(stream, dev))
+    with _on(dev):
+        st = lib().mf_moe_finalize_mxfp4(
+            _dev(expert_rows, torch.bfloat16, "expert_rows"), num_rows,
+            _dev(idx, torch.int32, "idx"),
+            _dev(weights, torch.float32, "weights", (T, k)),
+            _dev(residual, torch.float32, "residual", (T, H)),
+            _dev(residual_out, torch.float32, "residual_out", (T, H)),
+            _dev(gamma, torch.bfloat16, "gamma", (H,)), float(eps),
+            _dev(q, torch.uint8, "q", (T, H // 2)),
+            _dev(scales, torch.uint8, "scales", (T, H // 32)),
+            T, H, k, _stream(stream, dev))
     _check("mf_moe_finalize_mxfp4", st)
     return q, scales, residual_out
