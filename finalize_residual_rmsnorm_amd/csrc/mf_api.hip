@@ -387,8 +387,8 @@ const char* mf_status_string(int status) {
         case MF_ERR_UNSUPPORTED: return "MF_ERR_UNSUPPORTED: width, expert count or top-k not supported";
         case MF_ERR_ALIGN: return "MF_ERR_ALIGN: a pointer is misaligned";
         case MF_ERR_ALIAS: return "MF_ERR_ALIAS: an output overlaps an input";
-        case MF_ERR_VALUE: return "MF_ERR_VALUE: eps must be finite and >= 0";
         case MF_ERR_HIP: return "MF_ERR_HIP: the HIP runtime rejected the launch";
+        case MF_ERR_VALUE: return "MF_ERR_VALUE: eps must be finite and >= 0";
         default: return "unknown mf_status";
     }
 }

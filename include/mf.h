@@ -49,8 +49,8 @@ typedef enum mf_status {
     MF_ERR_UNSUPPORTED = -3, /* a width or top-k outside what the *_supported queries accept */
     MF_ERR_ALIGN = -4,       /* a pointer is not aligned as stated above */
     MF_ERR_ALIAS = -5,       /* an output overlaps an input (except residual_out == residual) */
-    MF_ERR_VALUE = -6,       /* eps is negative, NaN or infinite */
-    MF_ERR_HIP = -7          /* the HIP runtime reported an error for the launch */
+    MF_ERR_HIP = -6,         /* the HIP runtime reported an error for the launch */
+    MF_ERR_VALUE = -7        /* eps is negative, NaN or infinite */
 } mf_status;
 
 /*

@@ -11,7 +11,8 @@ import finalize_residual_rmsnorm_amd as mf
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mf.h")
 
-OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, VALUE, HIP = 0, -1, -2, -3, -4, -5, -6, -7
+# the numbering of the survey's proposed header, with MF_ERR_VALUE appended
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, HIP, VALUE = 0, -1, -2, -3, -4, -5, -6, -7
 
 # Fake device addresses: never dereferenced, every call below fails validation first.
 A = 0x7F0000000000
@@ -36,8 +37,18 @@ def test_header_symbols_are_exported():
         assert hasattr(L, n), n
 
 
+def test_status_numbering_matches_the_header():
+    text = open(HEADER).read()
+    declared = {m[0]: int(m[1]) for m in re.findall(r"(MF_\w+)\s*=\s*(-?\d+)", text)}
+    assert declared == dict(MF_OK=OK, MF_ERR_NULL=NULL, MF_ERR_SHAPE=SHAPE,
+                            MF_ERR_UNSUPPORTED=UNSUP, MF_ERR_ALIGN=ALIGN, MF_ERR_ALIAS=ALIAS,
+                            MF_ERR_HIP=HIP, MF_ERR_VALUE=VALUE)
+    assert mf.mf_status_string(HIP).startswith("MF_ERR_HIP")
+    assert mf.mf_status_string(VALUE).startswith("MF_ERR_VALUE")
+
+
 def test_status_strings_cover_every_code():
-    for code in (OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, VALUE, HIP):
+    for code in (OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, HIP, VALUE):
         s = mf.mf_status_string(code)
         assert s.startswith("MF_"), (code, s)
     assert mf.mf_status_string(12345) == "unknown mf_status"
@@ -319,3 +330,4 @@ def test_route_workspace_bytes():
     assert mf.lib().mf_moe_route_workspace_bytes(8, 0, 1) == UNSUP
     with pytest.raises(mf.MFError):
         f(8, 4, 5)
+
