@@ -26,11 +26,13 @@ __all__ = [
     "mf_gated_residual_next_rmsnorm", "mf_gated_residual_next_rmsnorm_supported",
     "mf_moe_finalize_ep_partial", "mf_moe_finalize_ep_combine", "mf_mxfp4_quantize",
     "mf_rmsnorm_mxfp4_quantize", "mf_mxfp4_supported", "mf_moe_finalize_mxfp4", "LIB_PATH",
+    "mf_moe_route_noalloc", "MF_ROUTE_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmf.so")
 
 MF_OK = 0
+MF_ROUTE_SCRATCH_BYTES = 4 << 20   # the static scratch of mf_moe_route_noalloc, per GPU
 _lib = None
 
 
@@ -73,6 +75,7 @@ def lib() -> ctypes.CDLL:
             "mf_moe_finalize_mxfp4": [p, i64, p, p, p, p, p, f32, p, p, i64, i32, i32, p],
             "mf_moe_route_supported": [i32, i32],
             "mf_moe_route_workspace_bytes": [i64, i32, i32],
+            "mf_moe_route_noalloc": [p, i64, i32, i32, p, p, p, p, p, p],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -382,6 +385,24 @@ def mf_moe_route(logits: torch.Tensor, k: int, *, expert_ids: torch.Tensor | Non
             _dev(offsets, torch.int32, "offsets", (E + 1,)),
             _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream, dev))
     _check("mf_moe_route", st)
+    return expert_ids, weights, idx, perm, offsets
+
+
+def mf_moe_route_noalloc(logits: torch.Tensor, k: int, *, expert_ids: torch.Tensor,
+                         weights: torch.Tensor, idx: torch.Tensor, perm: torch.Tensor,
+                         offsets: torch.Tensor, stream=None):
+    """mf_moe_route on the library's static scratch: no workspace, and the caller passes every
+    output (nothing is allocated).  Returns the outputs it was given."""
+    T, E = logits.shape
+    dev = logits.device
+    with _on(dev):
+        st = lib().mf_moe_route_noalloc(
+            _dev(logits, torch.float32, "logits"), T, E, k,
+            _dev(expert_ids, torch.int32, "expert_ids", (T, k)),
+            _dev(weights, torch.float32, "weights", (T, k)), _dev(idx, torch.int32, "idx", (T, k)),
+            _dev(perm, torch.int32, "perm", (T * k,)),
+            _dev(offsets, torch.int32, "offsets", (E + 1,)), _stream(stream, dev))
+    _check("mf_moe_route_noalloc", st)
     return expert_ids, weights, idx, perm, offsets
 
 

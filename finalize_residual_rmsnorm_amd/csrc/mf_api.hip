@@ -389,6 +389,8 @@ const char* mf_status_string(int status) {
         case MF_ERR_ALIAS: return "MF_ERR_ALIAS: an output overlaps an input";
         case MF_ERR_HIP: return "MF_ERR_HIP: the HIP runtime rejected the launch";
         case MF_ERR_VALUE: return "MF_ERR_VALUE: eps must be finite and >= 0";
+        case MF_ERR_SCRATCH:
+            return "MF_ERR_SCRATCH: the problem needs more scratch than the library's static buffer holds";
         default: return "unknown mf_status";
     }
 }

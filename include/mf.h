@@ -50,7 +50,9 @@ typedef enum mf_status {
     MF_ERR_ALIGN = -4,       /* a pointer is not aligned as stated above */
     MF_ERR_ALIAS = -5,       /* an output overlaps an input (except residual_out == residual) */
     MF_ERR_HIP = -6,         /* the HIP runtime reported an error for the launch */
-    MF_ERR_VALUE = -7        /* eps is negative, NaN or infinite */
+    MF_ERR_VALUE = -7,       /* eps is negative, NaN or infinite */
+    MF_ERR_SCRATCH = -8      /* the problem needs more scratch than the library's static
+                                buffer holds (mf_moe_route_noalloc only) */
 } mf_status;
 
 /*
@@ -237,6 +239,26 @@ int mf_moe_route(const float* logits, int64_t T, int32_t num_experts, int32_t k,
  * negative mf_status for unsupported arguments.
  */
 int64_t mf_moe_route_workspace_bytes(int64_t T, int32_t num_experts, int32_t k);
+
+/*
+ * mf_moe_route without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * results as mf_moe_route, bit for bit, with the per-block count table kept in a static device
+ * array of the library, MF_ROUTE_SCRATCH_BYTES (4 MiB) per GPU, held until the process ends.
+ *  - Arguments, outputs and checks as mf_moe_route's, less the workspace.  A call whose
+ *    mf_moe_route_workspace_bytes exceeds MF_ROUTE_SCRATCH_BYTES returns MF_ERR_SCRATCH and
+ *    launches nothing (at E = 256, k = 8 that is T above about a million tokens).
+ *  - Calls nothing that allocates (no hipMalloc, hipFree or allocating library routine).  The
+ *    first call on a device looks up that device's copy of the array (hipGetSymbolAddress);
+ *    a failure there returns MF_ERR_HIP.
+ *  - Every call on one GPU shares that GPU's array, and nothing in it needs to start at zero.
+ *    Calls that may overlap on one GPU (different streams, or several host threads) race on
+ *    it: the caller must order them, or use mf_moe_route with workspaces of its own.
+ */
+#define MF_ROUTE_SCRATCH_BYTES (4 << 20)
+int mf_moe_route_noalloc(const float* logits, int64_t T, int32_t num_experts, int32_t k,
+                         int32_t* expert_ids, float* weights, int32_t* idx, int32_t* perm,
+                         int32_t* expert_offsets, void* stream);
 
 /*
  * Capability queries (the fixed-width contract of [PR6544]'s "Fixed-Width Fused Norms":

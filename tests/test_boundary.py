@@ -11,8 +11,8 @@ import finalize_residual_rmsnorm_amd as mf
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mf.h")
 
-# the numbering of the survey's proposed header, with MF_ERR_VALUE appended
-OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, HIP, VALUE = 0, -1, -2, -3, -4, -5, -6, -7
+# the numbering of the survey's proposed header, with MF_ERR_VALUE and MF_ERR_SCRATCH appended
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, HIP, VALUE, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 # Fake device addresses: never dereferenced, every call below fails validation first.
 A = 0x7F0000000000
@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported():
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     L = ctypes.CDLL(mf.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -42,13 +42,13 @@ def test_status_numbering_matches_the_header():
     declared = {m[0]: int(m[1]) for m in re.findall(r"(MF_\w+)\s*=\s*(-?\d+)", text)}
     assert declared == dict(MF_OK=OK, MF_ERR_NULL=NULL, MF_ERR_SHAPE=SHAPE,
                             MF_ERR_UNSUPPORTED=UNSUP, MF_ERR_ALIGN=ALIGN, MF_ERR_ALIAS=ALIAS,
-                            MF_ERR_HIP=HIP, MF_ERR_VALUE=VALUE)
+                            MF_ERR_HIP=HIP, MF_ERR_VALUE=VALUE, MF_ERR_SCRATCH=SCRATCH)
     assert mf.mf_status_string(HIP).startswith("MF_ERR_HIP")
     assert mf.mf_status_string(VALUE).startswith("MF_ERR_VALUE")
 
 
 def test_status_strings_cover_every_code():
-    for code in (OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, HIP, VALUE):
+    for code in (OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, HIP, VALUE, SCRATCH):
         s = mf.mf_status_string(code)
         assert s.startswith("MF_"), (code, s)
     assert mf.mf_status_string(12345) == "unknown mf_status"
@@ -331,3 +331,27 @@ def test_route_workspace_bytes():
     with pytest.raises(mf.MFError):
         f(8, 4, 5)
 
+
+def route_noalloc(logits=A, T=16, E=64, k=4, ids=B, w=C, idx=D, perm=E_, off=F):
+    return mf.lib().mf_moe_route_noalloc(logits, T, E, k, ids, w, idx, perm, off, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), SHAPE), (dict(E=0), UNSUP), (dict(E=1025), UNSUP), (dict(k=17), UNSUP),
+    (dict(T=1 << 28, k=8), SHAPE),
+    (dict(T=2_000_000, E=256, k=8), SCRATCH),  # 8 MB of counts: beyond the 4 MiB scratch
+    (dict(off=None), NULL), (dict(logits=None), NULL), (dict(perm=None), NULL),
+    (dict(idx=D + 2), ALIGN), (dict(idx=B + 8), ALIAS), (dict(off=A + 4), ALIAS),
+])
+def test_route_noalloc_rejects_bad_arguments(kw, code):
+    # every check runs before the scratch lookup, the call's only HIP query
+    assert route_noalloc(**kw) == code
+
+
+def test_route_noalloc_scratch_limit():
+    f = mf.mf_moe_route_workspace_bytes
+    assert f(16384, 256, 8) <= mf.MF_ROUTE_SCRATCH_BYTES
+    assert f(1_000_000, 256, 8) <= mf.MF_ROUTE_SCRATCH_BYTES < f(1_100_000, 256, 8)
+    hdr = open(HEADER).read()
+    assert re.search(r"#define MF_ROUTE_SCRATCH_BYTES \(4 << 20\)", hdr)
+    assert mf.MF_ROUTE_SCRATCH_BYTES == 4 << 20
