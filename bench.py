@@ -4,20 +4,27 @@
 
 A step is one pass of the path over one batch of seeded synthetic inputs already resident
 in HBM: for the default workload, one mf_moe_finalize launch at T=16384, H=7168, E=256,
-k=8 (rows grouped by expert), which gathers the k rows, accumulates them in fp32, adds and
-stores the residual and emits the RMSNorm output.  W untimed steps, then exactly K timed
-steps between device synchronisations; one JSON line on stdout.
+k=8, which gathers the k rows, accumulates them in fp32, adds and stores the residual and
+emits the RMSNorm output.  The inputs follow the configured recipe: router logits ~ N(0, 1),
+routed on the GPU by mf_moe_route (top-8, softmax over the 8, rows stably sorted by expert id)
+before the timed region.  W untimed steps, then exactly K timed steps between device
+synchronisations; one JSON line on stdout.
 
-roofline: algorithmic HBM bytes of one launch / the kernel's average duration, timed
-with HIP events around every launch on the stream the kernel runs on; peak 8 TB/s.
-traffic: HBM bytes per launch measured with rocprofv3 counters, read from the committed
-summary under profiles/ when it was taken from the current kernel sources, else null.
-cpu_baseline: the CPU oracle timed on a bounded sample of the same workload on the host.
-Other workloads (--workload) time the sibling kernels (the gated norms, single and dual output,
-and the per-head norm), RMSNorm + MXFP4 quantisation, the expert-parallel partial and combine
-steps, the routing producer (one step = one
-mf_moe_route call: its three kernels, timed together by the events around the call) and the
-copy used for calibration.
+Timing: a calibrated spin kernel first keeps the GPU busy while the K launches, each between
+two HIP events on the launch stream, are enqueued, so the GPU runs them back to back and the
+events bracket the kernels, not the host's launch gaps.  value and ms_per_step come from the
+GPU time between the first launch's start event and the last launch's end event.
+roofline: algorithmic HBM bytes of one launch / the kernel's average event-timed duration;
+peak 8 TB/s.  traffic: HBM bytes per launch measured with rocprofv3 counters, read from the
+committed summary under profiles/ when it was taken from the current kernel sources, else null.
+cpu_baseline: the CPU oracle (with its own routing of the same logits) timed on a bounded
+sample of the workload on the host's CPU share; beside it, a sampled parity check of the GPU
+path against the oracle on the same inputs.
+Other workloads (--workload) time the one-token decode finalizes, the sibling kernels (the
+gated norms, single and dual output, and the per-head norm), RMSNorm + MXFP4 quantisation,
+the expert-parallel partial and combine steps, the routing producer (one step = one
+mf_moe_route call: its kernels, timed together by the events around the call) and the copy
+used for calibration.
 """
 from __future__ import annotations
 
@@ -25,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -36,6 +44,12 @@ sys.path.insert(0, ROOT)
 METRIC = "finalize tokens/s + achieved HBM GB/s (% of peak) at T=16384,H=7168,k=8"
 PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
+MAX_INPUT_SETS = 8192   # rotated copies of a small workload's inputs (cold data every step)
+WORKLOAD_CHOICES = ["finalize_prefill", "finalize_1tok", "finalize_1tok_per_expert",
+                    "finalize_decode_per_expert", "finalize_tiny", "gated_residual_rmsnorm",
+                    "gated_residual_next_rmsnorm", "rmsnorm_sigmoid_gate", "moe_route_prefill",
+                    "finalize_ep_partial", "finalize_ep_combine", "rmsnorm_mxfp4",
+                    "finalize_prefill_mxfp4", "moe_route_decode", "stream_copy"]
 CSRC = os.path.join(ROOT, "finalize_residual_rmsnorm_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -142,6 +156,20 @@ def make_workload(name: str) -> dict:
     if name == "stream_copy":
         return dict(kind="copy", bytes=1 << 30)
     return workloads.make_inputs(name)
+
+
+def route_on_gpu(d: dict, dev) -> dict:
+    """A finalize workload drawn with router logits, completed by the GPU routing call (expert
+    ids, weights and the expert-sorted idx), before any timing.  Other workloads pass through."""
+    if d.get("routing") != "logits":
+        return d
+    import torch
+
+    import finalize_residual_rmsnorm_amd as mf
+    import workloads
+    eids, w, idx, _, _ = mf.mf_moe_route(torch.from_numpy(d["logits"]).to(dev), d["k"])
+    torch.cuda.synchronize()
+    return workloads.with_routing(d, eids.cpu().numpy(), w.cpu().numpy(), idx.cpu().numpy())
 
 
 def upload(d: dict, dev):
@@ -263,21 +291,100 @@ def launch_config(name: str, d: dict) -> dict:
         pe = d.get("expert_gamma") is not None
         return mf.mf_launch_shape(mf.KIND_FINALIZE_PER_EXPERT if pe else mf.KIND_FINALIZE,
                                   d["T"], d["H"], d["k"])
-    if kind in ("ep_combine", "rmsnorm_mx"):
-        return mf.mf_launch_shape(mf.KIND_GATED, d["T"], d["H"])  # the same row shape
-    if kind in ("gated", "gated_next"):
-        return mf.mf_launch_shape(mf.KIND_GATED, d["T"], d["H"])
     if kind == "ep_combine":
         return mf.mf_launch_shape(mf.KIND_EP_COMBINE, d["T"], d["H"])
+    if kind in ("gated", "gated_next"):
+        return mf.mf_launch_shape(mf.KIND_GATED, d["T"], d["H"])
     return {}
 
 
 # ------------------------------------------------------------------------------ CPU oracle
 
 
-def cpu_baseline(d: dict, target_cpu_s: float = 20.0, max_threads: int = 16) -> dict:
-    """The CPU oracle on a bounded sample (about target_cpu_s of CPU work) of the workload's
-    tokens, split over up to max_threads host threads (the call releases the GIL)."""
+def cpu_share() -> int:
+    """Host threads this process may use: its CPU affinity, capped by OMP_NUM_THREADS when set
+    (a GPU machine allots each GPU a share of the host's cores and says so there)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
+def oracle_inputs(d: dict) -> dict:
+    """The workload as the oracle sees it: a logits-recipe finalize completed with the oracle's
+    own routing of the same logits (nothing the GPU computed enters the oracle)."""
+    if d.get("routing") != "logits":
+        return d
+    import oracle
+    import workloads
+    eids, w, idx, _, _ = oracle.moe_route(d["logits"], d["k"])
+    return workloads.with_routing(d, eids, w, idx)
+
+
+def parity_sample(d_raw: dict, d_gpu: dict, d_cpu: dict, dev, n: int = 256) -> dict:
+    """Parity of the timed path with the oracle on the bench's own inputs, before timing:
+    - routing (logits recipe): the GPU's expert ids and idx equal the oracle's;
+    - finalize: one launch on the oracle-routed inputs; on n sampled tokens (the first and the
+      last among them) residual_out bit-identical to the oracle's (plain finalize) or within
+      1e-6 + 1e-5 |r| (per-expert), and out within one bf16 ulp of the oracle's out (plain) or
+      of the oracle's RMSNorm of the GPU's residual_out (per-expert: the zero-weight finalize).
+    Other workloads: None (their parity is the GPU tests')."""
+    if d_raw["kind"] != "finalize":
+        return None
+    import torch
+
+    import oracle
+    rep = {}
+    if d_raw.get("routing") == "logits":
+        same_ids = bool(np.array_equal(d_gpu["expert_ids"], d_cpu["expert_ids"]))
+        same_idx = bool(np.array_equal(d_gpu["idx"], d_cpu["idx"]))
+        rep["routing_ids_and_idx_bit_identical"] = same_ids and same_idx
+    T = d_cpu["T"]
+    rng = np.random.default_rng(0)
+    tok = np.unique(np.concatenate([[0, T - 1], rng.choice(T, min(n, T), replace=False)]))
+    g = upload(d_cpu, dev)
+    launcher(d_cpu, g)()
+    torch.cuda.synchronize()
+    r_gpu = g["res_out"].cpu().numpy()[tok]
+    o_gpu = g["out"].view(torch.int16).cpu().numpy().view(np.uint16)[tok]
+    pe = d_cpu.get("expert_gamma") is not None
+    kw = dict(expert_ids=d_cpu["expert_ids"][tok], expert_gamma=d_cpu["expert_gamma"]) if pe else {}
+    r_ref, o_ref = oracle.moe_finalize(d_cpu["expert_rows"], d_cpu["idx"][tok],
+                                       d_cpu["weights"][tok], d_cpu["residual"][tok],
+                                       d_cpu["gamma"], d_cpu["eps"], **kw)
+    if pe:
+        r64 = r_ref.astype(np.float64)
+        rep["residual_out_within_tolerance"] = bool(
+            np.all(np.abs(r_gpu - r64) <= 1e-6 + 1e-5 * np.abs(r64)))
+        H = d_cpu["H"]
+        _, o_ref = oracle.moe_finalize(np.zeros((1, H), np.uint16),
+                                       np.zeros((len(tok), 1), np.int32),
+                                       np.zeros((len(tok), 1), np.float32), r_gpu,
+                                       d_cpu["gamma"], d_cpu["eps"])
+    else:
+        rep["residual_out_bit_identical"] = bool(np.array_equal(r_gpu, r_ref))
+
+    def ordered(b):
+        v = b.astype(np.int32)
+        return np.where(v & 0x8000, -(v & 0x7FFF), v)
+
+    ulp = np.abs(ordered(o_gpu) - ordered(o_ref))
+    rep["out_max_bf16_ulp"] = int(ulp.max())
+    rep["out_bit_identical_fraction"] = float((ulp == 0).mean())
+    rep["tokens_checked"] = int(len(tok))
+    rep["ok"] = bool(all(v for k_, v in rep.items() if k_.endswith("identical") or
+                         k_.endswith("tolerance")) and ulp.max() <= 1)
+    return rep
+
+
+def cpu_baseline(d: dict, target_cpu_s: float = 20.0) -> dict:
+    """The CPU oracle as it stands on a bounded sample (about target_cpu_s of CPU work) of the
+    workload's tokens, split into token blocks over the host threads of this process's CPU
+    share (the call releases the GIL); and one thread on one such block."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
@@ -316,11 +423,7 @@ def cpu_baseline(d: dict, target_cpu_s: float = 20.0, max_threads: int = 16) -> 
                                            d["gamma"], d["eps"])
 
     T = d["T"]
-    try:
-        ncpu = len(os.sched_getaffinity(0))
-    except AttributeError:
-        ncpu = os.cpu_count() or 1
-    threads = max(1, min(max_threads, ncpu))
+    threads = cpu_share()
     probe = min(T, 64)
     t0 = time.perf_counter()
     run(0, probe)
@@ -331,7 +434,7 @@ def cpu_baseline(d: dict, target_cpu_s: float = 20.0, max_threads: int = 16) -> 
     spans = [(i, min(n, i + chunk)) for i in range(0, n, chunk)]
     # a sample smaller than the target (the whole workload) is run again until about the
     # target amount of CPU work is done, so the timing is not dominated by thread start-up
-    with ThreadPoolExecutor(threads) as ex:
+    with ThreadPoolExecutor(len(spans)) as ex:
         t0 = time.perf_counter()
         list(ex.map(lambda s: run(*s), spans))
         first = time.perf_counter() - t0
@@ -348,22 +451,85 @@ def cpu_baseline(d: dict, target_cpu_s: float = 20.0, max_threads: int = 16) -> 
         run(0, one)
     dt1 = time.perf_counter() - t0
     what = f"the first {n} of {T} tokens" if n < T else f"all {T} tokens"
-    return dict(value=n * reps / dt, unit="tokens/s", cores=min(threads, len(spans)), kind="oracle",
-                sample=f"{what} of the same inputs, {reps} pass(es), {len(spans)} threads over "
-                       f"token blocks, {dt:.1f} s wall",
+    host = host_cpu()
+    return dict(value=n * reps / dt, unit="tokens/s", cores=len(spans), kind="oracle",
+                sample=f"{what} of the same inputs (routed by the oracle), {reps} pass(es), "
+                       f"{len(spans)} threads over token blocks, {dt:.1f} s wall; the threads are "
+                       f"this process's CPU share ({threads} of the host's "
+                       f"{host['logical_cpus']} logical CPUs)",
                 value_1_thread=one * reps1 / dt1,
                 sample_1_thread=f"the first {one} tokens, {reps1} pass(es), {dt1:.1f} s",
-                cpu_model=cpu_model())
+                cpu_share=threads, host=host)
 
 
-def cpu_model() -> str:
+def host_cpu() -> dict:
+    """The host's CPU as lscpu reports it (model string, sockets, cores, logical CPUs)."""
+    info = {"logical_cpus": os.cpu_count()}
     try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
-    except OSError:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        keys = {"Model name": "model", "Socket(s)": "sockets",
+                "Core(s) per socket": "cores_per_socket", "Thread(s) per core": "threads_per_core",
+                "CPU(s)": "lscpu_cpus", "Vendor ID": "vendor"}
+        for line in out.splitlines():
+            if ":" in line:
+                k, v = line.split(":", 1)
+                if k.strip() in keys:
+                    info[keys[k.strip()]] = v.strip()
+    except (OSError, ValueError, subprocess.SubprocessError):
         pass
-    return "unknown"
+    if "model" not in info:
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    info["model"] = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            info["model"] = "unknown"
+    try:
+        info["physical_cores"] = int(info["sockets"]) * int(info["cores_per_socket"])
+    except (KeyError, ValueError):
+        pass
+    return info
+
+
+# ------------------------------------------------------------------------------ timing
+
+
+def spin_cycles_per_us() -> float:
+    """Clock cycles torch.cuda._sleep spins per microsecond (measured once with events)."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    cycles = 2_000_000
+    a.record()
+    torch.cuda._sleep(cycles)
+    b.record()
+    torch.cuda.synchronize()
+    return cycles / max(a.elapsed_time(b) * 1e3, 1.0)
+
+
+def timed_pass(launches, K: int, stream, enqueue_s_per_launch: float, cycles_per_us: float):
+    """K launches, each between two events on `stream`, enqueued behind a spin kernel long enough
+    to cover the host's enqueue time, so the GPU runs them back to back.  Returns (per-launch
+    event times in ms, GPU span from the first start event to the last end event in ms, host
+    wall time in s, whether the queue ran dry between two launches)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    spin_us = min(2e6, max(50.0, 2.0 * K * enqueue_s_per_launch * 1e6))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    torch.cuda._sleep(int(spin_us * cycles_per_us))
+    for i in range(K):
+        ev[i][0].record(stream)
+        launches[i % len(launches)]()
+        ev[i][1].record(stream)
+    enqueued = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = [a.elapsed_time(b) for a, b in ev]
+    span = ev[0][0].elapsed_time(ev[-1][1])
+    return kern, span, wall, enqueued * 1e6 > spin_us
 
 
 # ------------------------------------------------------------------------------ main
@@ -374,13 +540,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="finalize_prefill",
-                    choices=["finalize_prefill", "finalize_decode_per_expert", "finalize_tiny",
-                             "gated_residual_rmsnorm", "gated_residual_next_rmsnorm",
-                             "rmsnorm_sigmoid_gate", "moe_route_prefill", "finalize_ep_partial",
-                             "finalize_ep_combine", "rmsnorm_mxfp4", "finalize_prefill_mxfp4",
-                             "moe_route_decode", "stream_copy"])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="finalize_prefill", choices=WORKLOAD_CHOICES)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (its CPU timing and the sampled parity check)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode "
@@ -395,49 +557,55 @@ def main() -> int:
     dev = torch.device("cuda:0")
     print(f"# {torch.cuda.get_device_name(dev)}; generating {args.workload}", file=sys.stderr,
           flush=True)
-    d = make_workload(args.workload)
+    d_raw = make_workload(args.workload)
+    d = route_on_gpu(d_raw, dev)
     ws = algorithmic_bytes(d)
     # Working sets that fit in the 256 MB Infinity Cache are rotated over enough copies that
     # every step reads cold data.
-    nsets = 1 if ws >= 4 * MALL_BYTES else min(64, -(-4 * MALL_BYTES // ws))
+    nsets = 1 if ws >= 4 * MALL_BYTES else min(MAX_INPUT_SETS, -(-4 * MALL_BYTES // ws))
     sets = [upload(d, dev) for _ in range(nsets)]
     launches = [launcher(d, g) for g in sets]
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
-    print(f"# uploaded {nsets} input set(s) of {ws / 1e9:.3f} GB; warmup {args.warmup}",
+    print(f"# uploaded {nsets} input set(s) of {ws / 1e9:.6f} GB; warmup {args.warmup}",
           file=sys.stderr, flush=True)
 
-    for i in range(args.warmup):
+    parity = None
+    d_cpu = None
+    if not args.no_cpu_baseline and tokens_of(d):
+        d_cpu = oracle_inputs(d_raw)
+        parity = parity_sample(d_raw, d, d_cpu, dev)
+        print(f"# parity sample: {parity}", file=sys.stderr, flush=True)
+
+    W = max(1, args.warmup)
+    cycles_per_us = spin_cycles_per_us()
+    t0 = time.perf_counter()
+    for i in range(W):
         launches[i % nsets]()
+    enqueue_s = (time.perf_counter() - t0) / W
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record(stream)
-        launches[i % nsets]()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    # the timed region starts on the set after the warmup's last
+    order = launches[W % nsets:] + launches[:W % nsets]
+    kern_ms, span_ms, wall, drained = timed_pass(order, K, stream, enqueue_s, cycles_per_us)
     avg_kernel_s = float(np.mean(kern_ms)) / 1e3
-    ms_per_step = wall * 1e3 / K
+    ms_per_step = span_ms / K
 
     achieved = ws / avg_kernel_s / 1e9
     traffic = read_traffic(args.workload, d["kind"])
     tokens = tokens_of(d)
-    value = tokens * K / wall if tokens else ws * K / wall / 1e9
+    value = tokens * K / (span_ms / 1e3) if tokens else ws * K / (span_ms / 1e3) / 1e9
     unit = "tokens/s" if tokens else "GB/s"
     cfg = {k: d[k] for k in ("T", "H", "E", "k", "heads", "D") if k in d}
-    cfg = dict(workload=args.workload, **cfg, layout=_layout(args.workload),
+    cfg = dict(workload=args.workload, **cfg, routing=_routing(d_raw),
                algorithmic_bytes_per_step=ws, input_sets=nsets,
                launch=launch_config(args.workload, d),
+               kernel_ms_mean=float(np.mean(kern_ms)),
                kernel_ms_median=float(np.median(kern_ms)),
                kernel_ms_p10=float(np.percentile(kern_ms, 10)),
-               kernel_ms_p90=float(np.percentile(kern_ms, 90)))
+               kernel_ms_p90=float(np.percentile(kern_ms, 90)),
+               host_wall_ms_per_step=wall * 1e3 / K, queue_ran_dry=drained)
     res = {
         "metric": METRIC if args.workload == "finalize_prefill" else f"{args.workload} {unit}",
         "value": value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -446,16 +614,24 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_GBPS, "traffic": traffic},
     }
-    if not args.no_cpu_baseline and tokens:
+    if parity is not None:
+        res["parity"] = parity
+    if d_cpu is not None:
         print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(d)
+        res["cpu_baseline"] = cpu_baseline(d_cpu)
     print(json.dumps(res), flush=True)
-    return 0
+    return 0 if parity is None or parity["ok"] else 1
 
 
-def _layout(name: str):
-    import workloads
-    return workloads.WORKLOADS.get(name, {}).get("layout")
+def _routing(d: dict) -> str:
+    if d.get("routing") == "logits":
+        order = ("rows in a drawn random permutation" if d["layout"] == "random"
+                 else "rows stably sorted by expert id")
+        return (f"top-{d['k']} of N(0,1) router logits over {d['E']} experts, softmax over the "
+                f"{d['k']}, routed on the GPU by mf_moe_route; {order}")
+    if d.get("routing") == "drawn":
+        return "drawn (uniform distinct experts, simplex weights)"
+    return None
 
 
 if __name__ == "__main__":

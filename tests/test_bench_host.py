@@ -1,5 +1,6 @@
 """Host-side checks of bench.py (no GPU): the algorithmic byte counts behind roofline.achieved,
-the source-keyed HBM traffic summaries, and the one-GPU refusal."""
+the source-keyed HBM traffic summaries, the launch shapes it reports, the host CPU report of
+the oracle leg, the routing recipe of the named workloads, and the one-GPU refusal."""
 import os
 import subprocess
 import sys
@@ -52,3 +53,40 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_launch_shape_reported_per_kernel():
+    # the combine has its own shape (at most 8 waves per token), not the gated norm's
+    comb = bench.launch_config("finalize_ep_combine", dict(kind="ep_combine", T=2048, H=7168))
+    gated = bench.launch_config("gated_residual_rmsnorm", dict(kind="gated", T=4096, H=7168))
+    fin = bench.launch_config("finalize_prefill", dict(kind="finalize", T=16384, H=7168, k=8,
+                                                       expert_gamma=None))
+    assert comb["waves_per_token"] == 8 and comb["vectors_per_lane"] == 2
+    assert gated["waves_per_token"] == 16 and gated["vectors_per_lane"] == 1
+    assert fin["waves_per_token"] == 16 and fin["block"] == 1024 and fin["grid"] == 16384
+
+
+def test_cpu_share_and_host_report(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
+    assert bench.cpu_share() == min(3, len(os.sched_getaffinity(0)))
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.cpu_share() == len(os.sched_getaffinity(0))
+    h = bench.host_cpu()
+    assert h["logical_cpus"] == os.cpu_count()
+    assert h["model"] and h["model"] != "unknown"
+
+
+def test_named_finalize_workloads_follow_the_logits_recipe():
+    import workloads
+    for name in ("finalize_tiny", "finalize_decode_per_expert", "finalize_prefill",
+                 "finalize_1tok", "finalize_1tok_per_expert", "finalize_ep_partial",
+                 "finalize_prefill_mxfp4"):
+        assert workloads.WORKLOADS[name]["routing"] == "logits", name
+    assert workloads.WORKLOADS["finalize_tiny"]["layout"] == "random"
+    assert workloads.WORKLOADS["finalize_prefill"]["layout"] == "expert_sorted"
+    # the bench's description of the recipe, and the oracle leg's own routing of the logits
+    d = workloads.make_inputs("finalize_prefill", T=64)
+    assert "routed on the GPU by mf_moe_route" in bench._routing(d)
+    c = bench.oracle_inputs(d)
+    assert c["idx"].shape == (64, 8) and c["weights"].dtype == np.float32
+    assert np.array_equal(np.sort(c["idx"].ravel()), np.arange(64 * 8))

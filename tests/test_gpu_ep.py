@@ -19,6 +19,7 @@ import torch
 import finalize_residual_rmsnorm_amd as mf
 import oracle
 import workloads
+from tests import refs
 from tests.helpers import bf16_ulp_diff
 
 pytestmark = pytest.mark.gpu
@@ -172,8 +173,37 @@ def test_ep_pipeline_on_one_gpu(G):
         assert np.all(err <= (2 * k + G + 2) * 2.0 ** -24 * mag)
 
 
+@pytest.mark.parametrize("G", [1, 3])
+def test_ep_pipeline_per_expert(G):
+    """Per-expert partials of G simulated ranks, then the combine.  The normalised rows make the
+    fp32 result non-unique: residual_out is held to the per-expert finalize's bar against the
+    oracle's two steps, and out to one bf16 ulp of the oracle's RMSNorm of the GPU's own
+    residual_out."""
+    T, H, k = 65, 4096, 8
+    d = workloads.make_finalize_inputs(T, H, E=32, k=k, seed=750 + G, per_expert=True,
+                                       residual_std=2.0)
+    say(f"ep pipeline per-expert T={T} H={H} k={k} G={G}")
+    parts = torch.empty((G, T, H), dtype=torch.float32, device=DEV)
+    idxs = split(d, G)
+    for g, idx in enumerate(idxs):
+        partial_gpu(d, idx, per_expert=True, out=parts[g])
+    out, r = mf.mf_moe_finalize_ep_combine(parts, up(d["residual"]), up(d["gamma"], True),
+                                           d["eps"])
+    torch.cuda.synchronize()
+    ref_parts = np.stack([partial_ref(d, idx, per_expert=True) for idx in idxs])
+    r_ref, _ = oracle.moe_finalize_ep_combine(ref_parts, d["residual"], d["gamma"], d["eps"])
+    rg = r.cpu().numpy()
+    err = np.abs(rg.astype(np.float64) - r_ref)
+    assert np.all(err <= 1e-6 + 1e-5 * np.abs(r_ref.astype(np.float64)))
+    # the combine step alone is exact: the oracle's combine of the GPU's own partials
+    r_own, _ = oracle.moe_finalize_ep_combine(parts.cpu().numpy(), d["residual"], d["gamma"],
+                                              d["eps"])
+    assert np.array_equal(rg, r_own)
+    assert_bf16_close(bits(out), refs.rmsnorm_of(rg, d["gamma"], d["eps"]))
+
+
 def test_ep_partial_workload_full_size():
-    d = workloads.make_inputs("finalize_ep_partial")
+    d = refs.named("finalize_ep_partial")
     say(f"ep partial workload T=16384 H=7168 k=8, rank 0 of 8: {(d['idx'] >= 0).mean():.3f} of slots local")
     got = partial_gpu(d, d["idx"])
     torch.cuda.synchronize()

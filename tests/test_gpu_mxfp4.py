@@ -12,7 +12,7 @@ Bars:
     scales are bit-identical.
   - mf_moe_finalize_mxfp4: residual_out bit-identical to the oracle's finalize (the same fp32
     FMA chain as mf_moe_finalize); codes and scales to the band bar above, against the oracle's
-    RMSNorm + MXFP4 of that fp32 residual.
+    RMSNorm + MXFP4 of that fp32 residual.  The prefill workload is checked on every token.
 Each case prints its name and sizes before it runs.
 """
 import json
@@ -25,6 +25,7 @@ import torch
 import finalize_residual_rmsnorm_amd as mf
 import oracle
 import workloads
+from tests import refs
 
 pytestmark = pytest.mark.gpu
 
@@ -233,8 +234,25 @@ def test_finalize_mxfp4_agrees_with_two_steps():
 
 
 def test_finalize_mxfp4_workload_full_size():
-    d = workloads.make_inputs("finalize_prefill_mxfp4")
-    rows = np.sort(np.random.default_rng(962).choice(d["T"], 1024, replace=False))
-    rows[0], rows[-1] = 0, d["T"] - 1
-    say("finalize mxfp4 workload T=16384 H=7168 k=8, 1024 sampled rows")
-    check_finalize_mx(d, rows=rows)
+    """Every one of the 16384 tokens, checked in blocks of 2048; the oracle's finalize and its
+    RMSNorm + MXFP4 run over the blocks in host threads (each token's arithmetic is the same in
+    any block)."""
+    from concurrent.futures import ThreadPoolExecutor
+    d = refs.named("finalize_prefill_mxfp4")
+    T = d["T"]
+    say(f"finalize mxfp4 workload T={T} H=7168 k=8, all tokens")
+    q, sc, r = finalize_mx_gpu(d)
+    blocks = [np.arange(lo, min(lo + 2048, T)) for lo in range(0, T, 2048)]
+
+    def reference(rows):
+        r_ref, _ = oracle.moe_finalize(d["expert_rows"], d["idx"][rows], d["weights"][rows],
+                                       d["residual"][rows], d["gamma"], d["eps"])
+        q_ref, sc_ref = oracle.rmsnorm_f32_mxfp4_quantize(r_ref, d["gamma"], d["eps"])
+        return r_ref, q_ref, sc_ref
+
+    with ThreadPoolExecutor(len(blocks)) as ex:
+        expected = list(ex.map(reference, blocks))
+    for rows, (r_ref, q_ref, sc_ref) in zip(blocks, expected):
+        assert np.array_equal(r[rows].view(np.uint32), r_ref.view(np.uint32)), \
+            f"residual_out differs in tokens {rows[0]}..{rows[-1]}"
+        check_band(q[rows], sc[rows], q_ref, sc_ref, r_ref, d["gamma"], d["eps"])

@@ -4,14 +4,16 @@ Bars (from the finalize's determinism requirement and the stated tolerances):
   - plain finalize residual_out: bit-identical to the oracle (the fp32 FMA chain in fixed
     order has one correct result);
   - per-expert and gated residual_out: |gpu - ref| <= 1e-6 + 1e-5 * |ref| (rsqrt / exp
-    rounding makes the fp32 result non-unique);
+    rounding makes the fp32 result non-unique), with a floor on the bit-identical fraction;
   - bf16 outputs: within one bf16 ulp (two neighbours are both correct near a rounding
-    midpoint), and almost always bit-identical.  Where residual_out is not unique, its
-    allowed error passes through the RMSNorm into out, so there the bar is one ulp plus
-    that propagated amount, |gamma| * rms_scale * (1e-6 + 1e-5 * |r|): ~0.003 ulp for a
-    typical element, more only where |r| is near zero;
+    midpoint) and at least 99% bit-identical.  Where residual_out is unique (the plain
+    finalize) the reference is the oracle's out.  Where it is not, the reference is the
+    oracle's final RMSNorm of the GPU's own residual_out (tests/refs.py), which has itself
+    just passed the residual bar: the output step is then held to one ulp on its own, and
+    no residual tolerance leaks into the bf16 bar;
   - index handling: exact (covered by the bit-identical residual_out).
-Each case prints its name and launch shape before it runs.
+The named finalize workloads take their idx and weights from the oracle's routing of their
+router logits (tests/refs.py).  Each case prints its name and launch shape before it runs.
 """
 import numpy as np
 import pytest
@@ -20,6 +22,7 @@ import torch
 import finalize_residual_rmsnorm_amd as mf
 import oracle
 import workloads
+from tests import refs
 from tests.helpers import bf16_ulp_diff
 
 pytestmark = pytest.mark.gpu
@@ -49,28 +52,26 @@ def assert_bf16_close(gpu, ref, min_exact=0.99):
     assert (d == 0).mean() >= min_exact, f"bit-identical fraction {(d == 0).mean():.5f}"
 
 
-def assert_bf16_close_given_residual_tol(gpu, ref, r_ref, gamma, eps, min_exact=0.99):
-    """bf16 outputs of a non-unique fp32 residual: one ulp plus the propagated tolerance."""
-    og = workloads.bf16_bits_to_f32(gpu).astype(np.float64)
-    orf = workloads.bf16_bits_to_f32(ref).astype(np.float64)
-    r = r_ref.astype(np.float64)
-    scale = 1.0 / np.sqrt((r * r).mean(axis=-1, keepdims=True) + eps)
-    g = np.abs(workloads.bf16_bits_to_f32(gamma).astype(np.float64))
-    mag = np.maximum(np.abs(orf), 2.0 ** -126)
-    ulp = 2.0 ** (np.floor(np.log2(mag)) - 7)
-    allowed = ulp * 1.0001 + 1.01 * g * scale * (1e-6 + 1e-5 * np.abs(r))
-    err = np.abs(og - orf)
-    assert np.all(err <= allowed), f"{(err > allowed).sum()} outputs beyond the bar"
-    d = bf16_ulp_diff(gpu, ref)
-    assert (d == 0).mean() >= min_exact, f"bit-identical fraction {(d == 0).mean():.5f}"
-    say(f"    out: max {d.max()} ulp, {(d > 1).sum()} elements beyond 1 ulp (all near r = 0)")
-
-
-def assert_fp32_tol(gpu, ref):
+def assert_fp32_tol(gpu, ref, min_exact):
+    """The non-unique fp32 residual: within 1e-6 + 1e-5 |ref| everywhere, and at least
+    min_exact of it bit-identical (the floor sits below what the GPU measured)."""
     err = np.abs(gpu.astype(np.float64) - ref.astype(np.float64))
     tol = 1e-6 + 1e-5 * np.abs(ref.astype(np.float64))
     assert np.all(err <= tol), f"max err {err.max():.3e} ({(err > tol).sum()} over tolerance)"
-    say(f"    residual_out bit-identical fraction {(gpu == ref).mean():.5f}")
+    frac = (gpu == ref).mean()
+    say(f"    residual_out bit-identical fraction {frac:.5f}")
+    assert frac >= min_exact, f"bit-identical fraction {frac:.5f} below {min_exact}"
+
+
+def assert_out_given_residual(out_gpu, r_gpu, gamma, eps, o_ref=None):
+    """bf16 out of a non-unique residual: within one ulp of the oracle's RMSNorm of the GPU's own
+    residual_out (and, for information, its distance to the oracle's own out)."""
+    want = refs.rmsnorm_of(r_gpu, gamma, eps)
+    assert_bf16_close(out_gpu, want)
+    if o_ref is not None:
+        d = bf16_ulp_diff(out_gpu, o_ref)
+        say(f"    out vs the oracle's own out: max {d.max()} ulp, "
+            f"{(d == 0).mean():.5f} bit-identical")
 
 
 def finalize_gpu(d, per_expert=False, residual_out=None, out=None):
@@ -112,7 +113,7 @@ def shape_str(kind, T, H, k=1):
 
 
 def test_finalize_tiny_workload():
-    d = workloads.make_inputs("finalize_tiny")
+    d = refs.named("finalize_tiny")
     say(f"finalize_tiny T=16 H=1024 k=2: {shape_str(0, 16, 1024, 2)}")
     out, r = finalize_gpu(d)
     torch.cuda.synchronize()
@@ -150,7 +151,7 @@ def test_finalize_matches_oracle(T, H, k, layout):
 @pytest.fixture(scope="module")
 def prefill():
     say("generating the prefill workload T=16384 H=7168 E=256 k=8 (host, ~20 s)")
-    return workloads.make_inputs("finalize_prefill")
+    return refs.named("finalize_prefill")
 
 
 def test_finalize_prefill_full_size(prefill):
@@ -231,13 +232,14 @@ def test_zero_tokens_is_a_no_op():
 
 
 def test_finalize_decode_per_expert_workload():
-    d = workloads.make_inputs("finalize_decode_per_expert")
+    d = refs.named("finalize_decode_per_expert")
     say(f"finalize_decode_per_expert T=64 H=4096 k=8: {shape_str(1, 64, 4096, 8)}")
     out, r = finalize_gpu(d, per_expert=True)
     torch.cuda.synchronize()
     r_ref, o_ref = finalize_ref(d, per_expert=True)
-    assert_fp32_tol(r.cpu().numpy(), r_ref)
-    assert_bf16_close_given_residual_tol(bits(out), o_ref, r_ref, d["gamma"], d["eps"])
+    rg = r.cpu().numpy()
+    assert_fp32_tol(rg, r_ref, min_exact=0.5)
+    assert_out_given_residual(bits(out), rg, d["gamma"], d["eps"], o_ref)
 
 
 @pytest.mark.parametrize("T,H,k", [(1, 64, 1), (5, 520, 3), (33, 7168, 8), (2100, 7168, 8),
@@ -249,8 +251,9 @@ def test_per_expert_matches_oracle(T, H, k):
     out, r = finalize_gpu(d, per_expert=True)
     torch.cuda.synchronize()
     r_ref, o_ref = finalize_ref(d, per_expert=True)
-    assert_fp32_tol(r.cpu().numpy(), r_ref)
-    assert_bf16_close_given_residual_tol(bits(out), o_ref, r_ref, d["gamma"], d["eps"])
+    rg = r.cpu().numpy()
+    assert_fp32_tol(rg, r_ref, min_exact=0.5)
+    assert_out_given_residual(bits(out), rg, d["gamma"], d["eps"], o_ref)
 
 
 def test_per_expert_batch_invariance():
@@ -267,6 +270,11 @@ def test_per_expert_batch_invariance():
 
 # ----------------------------------------------------------------------------- gated
 
+# The gated residual is one fp32 FMA of sigmoid(gate) and x onto the residual; the GPU's sigmoid
+# (a hardware exp and an IEEE division) is within a few ulp of the exact one, so most elements
+# round to the same fp32 value.  Floor on the bit-identical fraction (measured well above it).
+GATED_MIN_EXACT = 0.7
+
 
 def gated_gpu(d, residual_out=None):
     return mf.mf_gated_residual_rmsnorm(up(d["x"], True), up(d["gate"], True), up(d["residual"]),
@@ -280,8 +288,9 @@ def test_gated_workload_full_size():
     torch.cuda.synchronize()
     r_ref, o_ref = oracle.gated_residual_rmsnorm(d["x"], d["gate"], d["residual"], d["gamma"],
                                                  d["eps"])
-    assert_fp32_tol(r.cpu().numpy(), r_ref)
-    assert_bf16_close_given_residual_tol(bits(out), o_ref, r_ref, d["gamma"], d["eps"])
+    rg = r.cpu().numpy()
+    assert_fp32_tol(rg, r_ref, min_exact=GATED_MIN_EXACT)
+    assert_out_given_residual(bits(out), rg, d["gamma"], d["eps"], o_ref)
 
 
 @pytest.mark.parametrize("T,H", [(1, 8), (3, 520), (5000, 1024), (7, 32768), (2049, 8192),
@@ -293,8 +302,9 @@ def test_gated_matches_oracle(T, H):
     torch.cuda.synchronize()
     r_ref, o_ref = oracle.gated_residual_rmsnorm(d["x"], d["gate"], d["residual"], d["gamma"],
                                                  d["eps"])
-    assert_fp32_tol(r.cpu().numpy(), r_ref)
-    assert_bf16_close_given_residual_tol(bits(out), o_ref, r_ref, d["gamma"], d["eps"])
+    rg = r.cpu().numpy()
+    assert_fp32_tol(rg, r_ref, min_exact=GATED_MIN_EXACT)
+    assert_out_given_residual(bits(out), rg, d["gamma"], d["eps"], o_ref)
 
 
 def test_gated_zero_gate_is_exact():
@@ -331,9 +341,10 @@ def check_gated_next(d):
     torch.cuda.synchronize()
     r_ref, o_ref, on_ref = oracle.gated_residual_next_rmsnorm(
         d["x"], d["gate"], d["residual"], d["gamma"], d["gamma_next"], d["eps"])
-    assert_fp32_tol(r.cpu().numpy(), r_ref)
-    assert_bf16_close_given_residual_tol(bits(out), o_ref, r_ref, d["gamma"], d["eps"])
-    assert_bf16_close_given_residual_tol(bits(on), on_ref, r_ref, d["gamma_next"], d["eps"])
+    rg = r.cpu().numpy()
+    assert_fp32_tol(rg, r_ref, min_exact=GATED_MIN_EXACT)
+    assert_out_given_residual(bits(out), rg, d["gamma"], d["eps"], o_ref)
+    assert_out_given_residual(bits(on), rg, d["gamma_next"], d["eps"], on_ref)
     return out, on, r
 
 

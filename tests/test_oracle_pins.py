@@ -160,6 +160,21 @@ def test_finalize_zero_weights_keep_residual():
     assert _close_bf16(o, _rmsnorm_bits(d["residual"], d["gamma"], d["eps"]))
 
 
+def test_rmsnorm_of_a_given_residual():
+    # tests/refs.rmsnorm_of (the GPU tests' reference for the bf16 output of a non-unique fp32
+    # residual) is the zero-weight finalize: textbook RMSNorm of the residual it is given, over
+    # the rows of any leading shape, also when it runs over token blocks in threads
+    from tests import refs
+    rng = np.random.default_rng(21)
+    for T, H in ((1, 8), (37, 520), (300, 4096)):
+        r = rng.standard_normal((T, H), dtype=np.float32) * np.float32(2.0)
+        gamma = workloads.to_bf16_bits(1 + 0.1 * rng.standard_normal(H, dtype=np.float32))
+        got = refs.rmsnorm_of(r, gamma, 1e-6)
+        assert _close_bf16(got, _rmsnorm_bits(r, gamma, 1e-6))
+        assert np.array_equal(got, refs.rmsnorm_of(r, gamma, 1e-6, threads=1))
+        assert np.array_equal(refs.rmsnorm_of(r.reshape(1, T, H), gamma, 1e-6)[0], got)
+
+
 def test_finalize_unit_gamma_rms_closed_form():
     # gamma = 1: the RMS of r * (ms + eps)^-1/2 is sqrt(ms / (ms + eps)); bf16 rounding moves
     # each element by at most 2^-9 relative.

@@ -9,10 +9,49 @@ from tests.helpers import f32
 def test_same_seed_same_bytes():
     a = workloads.make_inputs("finalize_tiny")
     b = workloads.make_inputs("finalize_tiny")
-    for key in ("expert_rows", "idx", "weights", "expert_ids", "residual", "gamma"):
+    for key in ("logits", "expert_rows", "idx", "residual", "gamma"):
         assert np.array_equal(a[key], b[key]), key
     c = workloads.make_inputs("finalize_tiny", seed=99)
     assert not np.array_equal(a["expert_rows"], c["expert_rows"])
+    d = workloads.make_finalize_inputs(9, 16, E=4, k=2, seed=3)      # drawn routing
+    e = workloads.make_finalize_inputs(9, 16, E=4, k=2, seed=3)
+    for key in ("expert_rows", "idx", "weights", "expert_ids", "residual", "gamma"):
+        assert np.array_equal(d[key], e[key]), key
+
+
+def test_logits_recipe_draws_logits_and_leaves_the_routing_to_the_consumer():
+    # C1: N(0,1) logits [T, E], then a drawn random row permutation; the experts and weights are
+    # not drawn (the routing computes them)
+    d = workloads.make_inputs("finalize_tiny")
+    assert d["logits"].shape == (16, 8) and d["logits"].dtype == np.float32
+    assert d["expert_ids"] is None and d["weights"] is None
+    assert np.array_equal(np.sort(d["idx"].ravel()), np.arange(32))
+    # C3 at reduced T: the expert-sorted idx is the routing's too
+    p = workloads.make_inputs("finalize_prefill", T=4096)
+    assert p["idx"] is None and p["logits"].shape == (4096, 256)
+    assert abs(float(p["logits"].std()) - 1.0) < 0.01 and abs(float(p["logits"].mean())) < 0.01
+    assert p["expert_rows"].shape == (4096 * 8, 7168)
+
+
+def test_with_routing_completes_the_workload():
+    d = workloads.make_inputs("finalize_decode_per_expert", T=4)
+    ids = np.array([[3, 1, 0, 2, 4, 5, 6, 7]] * 4, np.int32)
+    w = np.full((4, 8), 0.125, np.float32)
+    idx = np.arange(32, dtype=np.int32).reshape(4, 8)[::-1].copy()
+    c = workloads.with_routing(d, ids, w, idx)
+    assert np.array_equal(c["expert_ids"], ids) and np.array_equal(c["idx"], idx)
+    assert d["expert_ids"] is None                                   # d is unchanged
+    # the random layout keeps its drawn permutation
+    t = workloads.make_inputs("finalize_tiny")
+    ct = workloads.with_routing(t, np.zeros((16, 2), np.int32), np.ones((16, 2), np.float32),
+                                np.zeros((16, 2), np.int32))
+    assert np.array_equal(ct["idx"], t["idx"])
+    # an expert-parallel view marks the other ranks' slots (expert e on rank e % 8)
+    ep = workloads.make_inputs("finalize_ep_partial", T=4)
+    ce = workloads.with_routing(ep, ids, w, idx)
+    assert np.array_equal(ce["idx"] >= 0, ids % 8 == 0)
+    with pytest.raises(ValueError):
+        workloads.with_routing(workloads.make_finalize_inputs(2, 8, E=4, k=2, seed=1), ids, w, idx)
 
 
 @pytest.mark.parametrize("layout", ["random", "expert_grouped"])
@@ -56,6 +95,7 @@ def test_route_inputs():
 
 def test_shapes_and_dtypes_of_named_workloads():
     d = workloads.make_inputs("finalize_decode_per_expert")
+    assert d["logits"].shape == (64, 128)
     assert d["expert_rows"].shape == (64 * 8, 4096) and d["expert_rows"].dtype == np.uint16
     assert d["expert_gamma"].shape == (128, 4096) and d["expert_gamma"].dtype == np.uint16
     assert d["residual"].dtype == np.float32 and abs(d["residual"].std() - 2.0) < 0.05
