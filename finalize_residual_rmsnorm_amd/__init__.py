@@ -26,7 +26,7 @@ __all__ = [
     "mf_gated_residual_next_rmsnorm", "mf_gated_residual_next_rmsnorm_supported",
     "mf_moe_finalize_ep_partial", "mf_moe_finalize_ep_combine", "mf_mxfp4_quantize",
     "mf_rmsnorm_mxfp4_quantize", "mf_mxfp4_supported", "mf_moe_finalize_mxfp4", "LIB_PATH",
-    "mf_moe_route_noalloc", "MF_ROUTE_SCRATCH_BYTES",
+    "mf_moe_route_noalloc", "MF_ROUTE_SCRATCH_BYTES", "mf_empty_grid",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmf.so")
@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
             "mf_rmsnorm_sigmoid_gate_supported": [i32],
             "mf_launch_shape": [ci, i64, i32, i32, p, p, p, p],
             "mf_stream_copy": [p, p, i64, p],
+            "mf_empty_grid": [i64, i32, p],
             "mf_status_string": [ci],
             "mf_moe_route": [p, i64, i32, i32, p, p, p, p, p, p, i64, p],
             "mf_gated_residual_next_rmsnorm": [p, p, p, p, p, p, f32, p, p, i64, i32, p],
@@ -340,6 +341,14 @@ def mf_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     with _on(src.device):
         _check("mf_stream_copy", lib().mf_stream_copy(src.data_ptr(), dst.data_ptr(), n,
                                                       _stream(stream, src.device)))
+
+
+def mf_empty_grid(workgroups: int, threads: int, device=None, stream=None) -> None:
+    """Launch an empty kernel of `workgroups` x `threads` (a measurement aid: the dispatch floor
+    of a grid shape) on the current stream of `device` (default: the current device)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with _on(dev):
+        _check("mf_empty_grid", lib().mf_empty_grid(workgroups, threads, _stream(stream, dev)))
 
 
 def mf_moe_route_supported(num_experts: int, k: int) -> bool:

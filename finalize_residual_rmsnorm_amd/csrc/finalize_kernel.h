@@ -138,6 +138,9 @@ __device__ __forceinline__ void consume_batch(const GatherBatch<VPL, JB, PER_EXP
                                               int64_t tk, int jb, int k,
                                               const Slots<VPL, TAIL>& sl, TokenLds& L,
                                               const RowMap& m) {
+    // Per-expert: the row's scale inv = (mean(x_j^2) + eps)^-1/2, and the row enters the sum as
+    // fma(w_j * inv, x * gamma_e, acc): the product of two bf16 values is exact in fp32, so the
+    // only roundings are the scale's, its product with the weight and the fma's.
     float inv[JB];
     if constexpr (PER_EXPERT) {
 #pragma unroll
@@ -148,15 +151,17 @@ __device__ __forceinline__ void consume_batch(const GatherBatch<VPL, JB, PER_EXP
             inv[u] = lane_sumsq(x, sl);
         }
         token_sum<JB>(inv, L, m);
+        const float inv_h = 1.0f / (float)a.H;
 #pragma unroll
-        for (int u = 0; u < JB; ++u) inv[u] = 1.0f / __builtin_sqrtf(inv[u] / (float)a.H + a.eps);
+        for (int u = 0; u < JB; ++u) inv[u] = rms_scale(inv[u], inv_h, a.eps);
     }
 #pragma unroll
     for (int u = 0; u < JB; ++u) {
         bool use = jb + u < k;
         if constexpr (SKIP) use = use && b.live[u];
         if (use) {
-            const float wj = a.w[tk + jb + u];
+            // (a skipped slot's weight is never read)
+            const float wj = PER_EXPERT ? a.w[tk + jb + u] * inv[u] : a.w[tk + jb + u];
 #pragma unroll
             for (int s = 0; s < VPL; ++s) {
                 float x[8];
@@ -165,8 +170,7 @@ __device__ __forceinline__ void consume_batch(const GatherBatch<VPL, JB, PER_EXP
                     float g[8];
                     widen8(b.g[u][s], g);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        acc[s][i] = __builtin_fmaf(wj, (x[i] * inv[u]) * g[i], acc[s][i]);
+                    for (int i = 0; i < 8; ++i) acc[s][i] = __builtin_fmaf(wj, x[i] * g[i], acc[s][i]);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) acc[s][i] = __builtin_fmaf(wj, x[i], acc[s][i]);
@@ -250,7 +254,7 @@ moe_finalize_kernel(const FinalizeArgs a) {
     if constexpr (OUT_MX) {
         float ss[1] = {lane_sumsq(acc, sl)};
         token_sum<1>(ss, L, m);
-        const float inv = 1.0f / __builtin_sqrtf(ss[0] / (float)H + a.eps);
+        const float inv = rms_scale(ss[0], 1.0f / (float)H, a.eps);
         mx_store_normed(acc, g, sl, inv, m.lane, a.q + m.t * (H / 2), a.scales + m.t * (H / 32));
     } else {
         rmsnorm_store(acc, g, sl, a.out + m.t * H, H, a.eps, L, m);

@@ -89,6 +89,14 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
+// The RMSNorm scale (mean + eps)^-1/2 of a row sum of squares: the mean as ss * (1/n) and the
+// hardware reciprocal square root.  Both are within a few fp32 ulps of the exact value, far
+// below half an ulp of the bf16 (or MXFP4) outputs the scale feeds, and a fixed function of ss:
+// the same ss always gives the same scale.
+__device__ __forceinline__ float rms_scale(float ss, float inv_n, float eps) {
+    return __builtin_amdgcn_rsqf(__builtin_fmaf(ss, inv_n, eps));
+}
+
 // Sum of squares of eight values in index order.
 __device__ __forceinline__ float sumsq8(const float (&x)[8]) {
     float s = x[0] * x[0];

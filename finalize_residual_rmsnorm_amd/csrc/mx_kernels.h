@@ -91,7 +91,7 @@ rmsnorm_mxfp4_kernel(const RmsMxArgs a) {
     float ss[1] = {lane_sumsq(x, sl)};
     TokenLds L = token_lds(lds, m.wpt, 1);
     token_sum<1>(ss, L, m);
-    const float inv = 1.0f / __builtin_sqrtf(ss[0] / (float)H + a.eps);
+    const float inv = rms_scale(ss[0], 1.0f / (float)H, a.eps);
     mx_store_normed(x, gm, sl, inv, m.lane, a.q + m.t * (H / 2), a.scales + m.t * (H / 32));
 }
 

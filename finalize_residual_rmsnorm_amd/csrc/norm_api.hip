@@ -19,7 +19,6 @@ using namespace mf;
 // One group of 8 heads per wave and one wave per workgroup: measured 7% faster on MI355X than
 // two groups per wave in 4-wave workgroups (every other combination of 1-2 groups and 64-1024
 // threads was within 1% of the latter).
-constexpr int kPerHeadGroupsPerWave = 1;
 
 template <int VPL, bool DUAL>
 const void* gated_fn(int tail) {
@@ -135,13 +134,9 @@ int mf_rmsnorm_sigmoid_gate(const uint16_t* x, const uint16_t* gate, const uint1
     if (T < 0 || num_heads < 1) return MF_ERR_SHAPE;
     if (!mf_rmsnorm_sigmoid_gate_supported(head_dim)) return MF_ERR_UNSUPPORTED;
     if (T == 0) return MF_OK;
-    constexpr int G = kPerHeadGroupsPerWave;
     const int64_t nh = T * num_heads;
     const int64_t groups = (nh + kHeadsPerWaveLoad - 1) / kHeadsPerWaveLoad;
-    const int64_t waves = (groups + G - 1) / G;
-    constexpr int WPB = kPerHeadBlock / kWave;
-    const int64_t blocks = (waves + WPB - 1) / WPB;
-    if (!grid_fits(blocks, kPerHeadBlock)) return MF_ERR_SHAPE;
+    if (!grid_fits(groups, kPerHeadBlock)) return MF_ERR_SHAPE;
     if (!x || !gate || !gamma || !out) return MF_ERR_NULL;
     if (!eps_ok(eps)) return MF_ERR_VALUE;
     if (!aligned(x, 16) || !aligned(gate, 16) || !aligned(gamma, 16) || !aligned(out, 16))
@@ -159,8 +154,11 @@ int mf_rmsnorm_sigmoid_gate(const uint16_t* x, const uint16_t* gate, const uint1
     a.num_heads_total = nh;
     a.eps = eps;
     void* args[] = {&a};
-    return hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&rmsnorm_sigmoid_gate_kernel<G>),
-                                      dim3((unsigned)blocks), dim3(kPerHeadBlock), args, 0,
+    // the full-tile kernel when the heads fill whole waves, else the one with the tail handling
+    const void* fn = nh % kHeadsPerWaveLoad == 0
+                         ? reinterpret_cast<const void*>(&rmsnorm_sigmoid_gate_kernel<false>)
+                         : reinterpret_cast<const void*>(&rmsnorm_sigmoid_gate_kernel<true>);
+    return hip_status(hipLaunchKernel(fn, dim3((unsigned)groups), dim3(kPerHeadBlock), args, 0,
                                       reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -179,6 +177,14 @@ int mf_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
     void* args[] = {&s, &d, const_cast<int64_t*>(&n)};
     return hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&stream_copy_kernel<U>),
                                       dim3((unsigned)blocks), dim3(256), args, 0,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+int mf_empty_grid(int64_t workgroups, int32_t threads, void* stream) {
+    if (workgroups < 1 || threads < 1 || threads > 1024) return MF_ERR_SHAPE;
+    if (!grid_fits(workgroups, threads)) return MF_ERR_SHAPE;
+    return hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&empty_grid_kernel),
+                                      dim3((unsigned)workgroups), dim3(threads), nullptr, 0,
                                       reinterpret_cast<hipStream_t>(stream)));
 }
 

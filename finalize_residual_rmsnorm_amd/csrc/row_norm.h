@@ -203,7 +203,7 @@ __device__ __forceinline__ void rmsnorm_store(const float (&r)[VPL][8], const u3
                                               int H, float eps, TokenLds& L, const RowMap& m) {
     float ss[1] = {lane_sumsq(r, sl)};
     token_sum<1>(ss, L, m);
-    const float inv = 1.0f / __builtin_sqrtf(ss[0] / (float)H + eps);
+    const float inv = rms_scale(ss[0], 1.0f / (float)H, eps);
 #pragma unroll
     for (int s = 0; s < VPL; ++s) {
         float gf[8];

@@ -288,6 +288,13 @@ int mf_launch_shape(int kind, int64_t T, int32_t H, int32_t k, int32_t* waves_pe
  */
 int mf_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
+/*
+ * An empty kernel of `workgroups` workgroups of `threads` threads (1..1024): a measurement aid
+ * giving the dispatch floor of a grid shape, e.g. the per-head norm's 32768 one-wave
+ * workgroups.  Returns MF_ERR_SHAPE for an empty or oversized grid.
+ */
+int mf_empty_grid(int64_t workgroups, int32_t threads, void* stream);
+
 /* Human-readable name of a status code (never NULL). */
 const char* mf_status_string(int status);
 

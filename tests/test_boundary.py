@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported():
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     L = ctypes.CDLL(mf.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -355,3 +355,12 @@ def test_route_noalloc_scratch_limit():
     hdr = open(HEADER).read()
     assert re.search(r"#define MF_ROUTE_SCRATCH_BYTES \(4 << 20\)", hdr)
     assert mf.MF_ROUTE_SCRATCH_BYTES == 4 << 20
+
+
+def test_empty_grid_rejects_bad_shapes():
+    g = mf.lib().mf_empty_grid
+    assert g(0, 64, None) == SHAPE
+    assert g(-5, 64, None) == SHAPE
+    assert g(8, 0, None) == SHAPE
+    assert g(8, 1025, None) == SHAPE
+    assert g(1 << 31, 1024, None) == SHAPE        # past the 32-bit work-item count
