@@ -10,12 +10,13 @@ routed on the GPU by mf_moe_route (top-8, softmax over the 8, rows stably sorted
 before the timed region.  W untimed steps, then exactly K timed steps between device
 synchronisations; one JSON line on stdout.
 
-Timing: a calibrated spin kernel first keeps the GPU busy while the K launches, each between
-two HIP events on the launch stream, are enqueued, so the GPU runs them back to back and the
-events bracket the kernels, not the host's launch gaps.  value and ms_per_step come from the
-GPU time between the first launch's start event and the last launch's end event.
-roofline: algorithmic HBM bytes of one launch / the kernel's average event-timed duration;
-peak 8 TB/s.  traffic: HBM bytes per launch measured with rocprofv3 counters, read from the
+Timing: a calibrated spin kernel first keeps the GPU busy while the K launches are enqueued on
+the launch stream, so the GPU runs them back to back, and two HIP events on that stream bracket
+the K launches: the kernels' time, not the host's launch gaps.  value, ms_per_step and the
+kernel's average launch duration come from that span.  A second pass puts an event pair around
+every launch for the spread (p10/median/p90; each pair adds its own few microseconds).
+roofline: algorithmic HBM bytes of one launch / the kernel's average launch duration; peak
+8 TB/s.  traffic: HBM bytes per launch measured with rocprofv3 counters, read from the
 committed summary under profiles/ when it was taken from the current kernel sources, else null.
 cpu_baseline: the CPU oracle (with its own routing of the same logits) timed on a bounded
 sample of the workload on the host's CPU share; beside it, a sampled parity check of the GPU
@@ -49,7 +50,8 @@ WORKLOAD_CHOICES = ["finalize_prefill", "finalize_1tok", "finalize_1tok_per_expe
                     "finalize_decode_per_expert", "finalize_tiny", "gated_residual_rmsnorm",
                     "gated_residual_next_rmsnorm", "rmsnorm_sigmoid_gate", "moe_route_prefill",
                     "finalize_ep_partial", "finalize_ep_combine", "rmsnorm_mxfp4",
-                    "finalize_prefill_mxfp4", "moe_route_decode", "stream_copy"]
+                    "finalize_prefill_mxfp4", "moe_route_decode", "stream_copy",
+                    "stream_copy_per_head", "empty_grid_per_head"]
 CSRC = os.path.join(ROOT, "finalize_residual_rmsnorm_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -141,6 +143,8 @@ def algorithmic_bytes(d: dict) -> int:
         return n * 6 + d["D"] * 2
     if kind == "copy":
         return 2 * d["bytes"]
+    if kind == "empty_grid":
+        return 0
     if kind == "route":
         T, E, k = d["T"], d["E"], d["k"]
         return T * E * 4 + T * k * 16 + (E + 1) * 4   # logits in; ids, weights, idx, perm out
@@ -151,10 +155,20 @@ def tokens_of(d: dict) -> int:
     return d["T"] if "T" in d else 0
 
 
+# The per-head norm's bytes (4096 tokens x 64 heads x 64 values: x and gate read, out written)
+PER_HEAD_BYTES = 4096 * 64 * 64 * 6 + 64 * 2
+
+
 def make_workload(name: str) -> dict:
     import workloads
     if name == "stream_copy":
         return dict(kind="copy", bytes=1 << 30)
+    if name == "stream_copy_per_head":
+        # a plain copy moving the per-head norm's byte count (half read, half written)
+        return dict(kind="copy", bytes=PER_HEAD_BYTES // 2 // 16 * 16)
+    if name == "empty_grid_per_head":
+        # an empty kernel of the per-head norm's grid: 8 heads per one-wave workgroup
+        return dict(kind="empty_grid", workgroups=4096 * 64 // 8, threads=64)
     return workloads.make_inputs(name)
 
 
@@ -231,6 +245,8 @@ def upload(d: dict, dev):
         n = d["bytes"] // 4
         return dict(src=torch.randint(0, 1 << 30, (n,), dtype=torch.int32, device=dev),
                     dst=torch.empty(n, dtype=torch.int32, device=dev))
+    if kind == "empty_grid":
+        return {}
     if kind == "route":
         import finalize_residual_rmsnorm_amd as mf
         T, E, k = d["T"], d["E"], d["k"]
@@ -277,6 +293,8 @@ def launcher(d: dict, g: dict):
                                                   out=g["out"])
     if kind == "copy":
         return lambda: mf.mf_stream_copy(g["src"], g["dst"])
+    if kind == "empty_grid":
+        return lambda: mf.mf_empty_grid(d["workgroups"], d["threads"])
     if kind == "route":
         return lambda: mf.mf_moe_route(g["logits"], d["k"], expert_ids=g["eids"], weights=g["w"],
                                        idx=g["idx"], perm=g["perm"], offsets=g["off"],
@@ -508,28 +526,32 @@ def spin_cycles_per_us() -> float:
     return cycles / max(a.elapsed_time(b) * 1e3, 1.0)
 
 
-def timed_pass(launches, K: int, stream, enqueue_s_per_launch: float, cycles_per_us: float):
-    """K launches, each between two events on `stream`, enqueued behind a spin kernel long enough
-    to cover the host's enqueue time, so the GPU runs them back to back.  Returns (per-launch
-    event times in ms, GPU span from the first start event to the last end event in ms, host
-    wall time in s, whether the queue ran dry between two launches)."""
+def enqueue_behind_spin(launches, K: int, enqueue_s_per_launch: float, cycles_per_us: float,
+                        per_launch_events: bool, stream):
+    """K launches enqueued behind a spin kernel long enough to cover the host's enqueue time, so
+    the GPU runs them back to back.  Returns (event pairs, host wall seconds, whether the
+    enqueue outlasted the spin, i.e. the queue may have run dry)."""
     import torch
+    n_ev = K if per_launch_events else 1
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-    spin_us = min(2e6, max(50.0, 2.0 * K * enqueue_s_per_launch * 1e6))
+          for _ in range(n_ev)]
+    spin_us = min(2e6, max(50.0, 3.0 * K * enqueue_s_per_launch * 1e6))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     torch.cuda._sleep(int(spin_us * cycles_per_us))
+    if not per_launch_events:
+        ev[0][0].record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
+        if per_launch_events:
+            ev[i][0].record(stream)
         launches[i % len(launches)]()
-        ev[i][1].record(stream)
+        if per_launch_events:
+            ev[i][1].record(stream)
+    if not per_launch_events:
+        ev[0][1].record(stream)
     enqueued = time.perf_counter() - t0
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern = [a.elapsed_time(b) for a, b in ev]
-    span = ev[0][0].elapsed_time(ev[-1][1])
-    return kern, span, wall, enqueued * 1e6 > spin_us
+    return ev, time.perf_counter() - t0, enqueued * 1e6 > spin_us
 
 
 # ------------------------------------------------------------------------------ main
@@ -562,7 +584,7 @@ def main() -> int:
     ws = algorithmic_bytes(d)
     # Working sets that fit in the 256 MB Infinity Cache are rotated over enough copies that
     # every step reads cold data.
-    nsets = 1 if ws >= 4 * MALL_BYTES else min(MAX_INPUT_SETS, -(-4 * MALL_BYTES // ws))
+    nsets = 1 if ws == 0 or ws >= 4 * MALL_BYTES else min(MAX_INPUT_SETS, -(-4 * MALL_BYTES // ws))
     sets = [upload(d, dev) for _ in range(nsets)]
     launches = [launcher(d, g) for g in sets]
     stream = torch.cuda.current_stream(dev)
@@ -588,24 +610,35 @@ def main() -> int:
     K = args.steps
     # the timed region starts on the set after the warmup's last
     order = launches[W % nsets:] + launches[:W % nsets]
-    kern_ms, span_ms, wall, drained = timed_pass(order, K, stream, enqueue_s, cycles_per_us)
-    avg_kernel_s = float(np.mean(kern_ms)) / 1e3
+    # The timed region: K launches back to back between two events on the launch stream.
+    ev, wall, drained = enqueue_behind_spin(order, K, enqueue_s, cycles_per_us, False, stream)
+    span_ms = ev[0][0].elapsed_time(ev[0][1])
+    avg_kernel_s = span_ms / K / 1e3
     ms_per_step = span_ms / K
+    # The spread over launches, from a second pass with an event pair around every launch (each
+    # pair adds the events' own cost, a few microseconds, to every figure).
+    ev2, _, drained2 = enqueue_behind_spin(order, K, enqueue_s, cycles_per_us, True, stream)
+    kern_ms = [a.elapsed_time(b) for a, b in ev2]
 
     achieved = ws / avg_kernel_s / 1e9
-    traffic = read_traffic(args.workload, d["kind"])
+    traffic = read_traffic(args.workload, d["kind"]) if d["kind"] in KERNEL_SOURCES else None
     tokens = tokens_of(d)
-    value = tokens * K / (span_ms / 1e3) if tokens else ws * K / (span_ms / 1e3) / 1e9
-    unit = "tokens/s" if tokens else "GB/s"
-    cfg = {k: d[k] for k in ("T", "H", "E", "k", "heads", "D") if k in d}
+    if tokens:
+        value, unit = tokens * K / (span_ms / 1e3), "tokens/s"
+    elif ws:
+        value, unit = ws * K / (span_ms / 1e3) / 1e9, "GB/s"
+    else:
+        value, unit = K / (span_ms / 1e3), "launches/s"
+    cfg = {k: d[k] for k in ("T", "H", "E", "k", "heads", "D", "bytes", "workgroups", "threads")
+           if k in d}
     cfg = dict(workload=args.workload, **cfg, routing=_routing(d_raw),
                algorithmic_bytes_per_step=ws, input_sets=nsets,
                launch=launch_config(args.workload, d),
-               kernel_ms_mean=float(np.mean(kern_ms)),
-               kernel_ms_median=float(np.median(kern_ms)),
-               kernel_ms_p10=float(np.percentile(kern_ms, 10)),
-               kernel_ms_p90=float(np.percentile(kern_ms, 90)),
-               host_wall_ms_per_step=wall * 1e3 / K, queue_ran_dry=drained)
+               kernel_ms_avg_back_to_back=ms_per_step,
+               event_pair_ms_median=float(np.median(kern_ms)),
+               event_pair_ms_p10=float(np.percentile(kern_ms, 10)),
+               event_pair_ms_p90=float(np.percentile(kern_ms, 90)),
+               host_wall_ms_per_step=wall * 1e3 / K, queue_ran_dry=drained or drained2)
     res = {
         "metric": METRIC if args.workload == "finalize_prefill" else f"{args.workload} {unit}",
         "value": value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": args.warmup,
