@@ -11,6 +11,11 @@ The arithmetic lives in ``oracle.c`` (plain loops; FP32 FMA where the pages fix 
 precision, float64 everywhere else).  This module compiles it with gcc when the shared
 object is missing or older than its source, and wraps it for numpy arrays.
 bfloat16 arrays are ``numpy.uint16`` bit patterns.
+
+With ``ORACLE_SANITIZE=1`` in the environment the module builds and loads a separate copy,
+``liboracle_san.so``, compiled with AddressSanitizer and UndefinedBehaviorSanitizer (any
+undefined-behaviour report aborts); the process must then have gcc's ASan runtime preloaded
+(``LD_PRELOAD``).  tests/test_sanitizers.py runs the oracle's pins that way.
 """
 from __future__ import annotations
 
@@ -23,20 +28,32 @@ import numpy as np
 _DIR = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(_DIR, "oracle.c")
 LIB = os.path.join(_DIR, "liboracle.so")
+LIB_SAN = os.path.join(_DIR, "liboracle_san.so")
 # No fast-math and no contraction: every FMA in the source is an explicit fmaf().
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
           "-Wall", "-Wextra"]
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+             "-fno-omit-frame-pointer", "-g"]
 
 _lib = None
 
 
-def build(force: bool = False) -> str:
-    """Compile oracle.c into liboracle.so with gcc; returns the library path."""
-    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-        tmp = LIB + f".tmp{os.getpid()}"
-        subprocess.run(["gcc", *CFLAGS, "-o", tmp, SRC, "-lm"], check=True)
-        os.replace(tmp, LIB)
-    return LIB
+def sanitized() -> bool:
+    """Whether this process uses the ASan/UBSan build (ORACLE_SANITIZE=1)."""
+    return os.environ.get("ORACLE_SANITIZE", "") == "1"
+
+
+def build(force: bool = False, sanitize: bool | None = None) -> str:
+    """Compile oracle.c with gcc (the sanitized copy when asked, or when ORACLE_SANITIZE=1);
+    returns the library path."""
+    san = sanitized() if sanitize is None else sanitize
+    lib = LIB_SAN if san else LIB
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(SRC):
+        tmp = lib + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", *CFLAGS, *(SAN_FLAGS if san else []), "-o", tmp, SRC, "-lm"],
+                       check=True)
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
