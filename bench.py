@@ -47,6 +47,7 @@ PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
 MAX_INPUT_SETS = 8192   # rotated copies of a small workload's inputs (cold data every step)
 WORKLOAD_CHOICES = ["finalize_prefill", "finalize_1tok", "finalize_1tok_per_expert",
+                    "finalize_wide_12288", "finalize_wide_20480", "finalize_wide_32768",
                     "finalize_decode_per_expert", "finalize_tiny", "gated_residual_rmsnorm",
                     "gated_residual_next_rmsnorm", "rmsnorm_sigmoid_gate", "moe_route_prefill",
                     "finalize_ep_partial", "finalize_ep_combine", "rmsnorm_mxfp4",

@@ -35,7 +35,37 @@ RowShape combine_shape(int64_t T, int32_t H) {
     return s.vpl <= kMaxVpl ? s : row_shape(T, H, kMaxWaves, kMaxVpl);
 }
 
-RowShape finalize_shape(int64_t T, int32_t H, int32_t k, bool per_expert) {
+// Rows too wide for one or two slots per wave (H > 8192) take the slot-serial kernel
+// (moe_finalize_wide_kernel) at the compiled top-k when its shape fills whole waves of slots:
+// 8 waves per token up to 40 slots (H <= 20480), 16 beyond, measured fastest at H = 12288, 20480
+// and 32768.  Other wide shapes (a row that is not whole waves of whole slots, another top-k)
+// keep moe_finalize_kernel.
+constexpr int kWideMaxVpl = 5;
+
+RowShape wide_shape(int64_t T, int32_t H) {
+    const int ns = (H + kSlot - 1) / kSlot;
+    const int waves = ns <= 40 ? 8 : 16;
+    RowShape s;
+    s.vpl = (ns + waves - 1) / waves;
+    s.wpt = pow2_at_least((ns + s.vpl - 1) / s.vpl);
+    s.tail = H != ns * kSlot ? kRowRagged : (ns == s.wpt * s.vpl ? kRowFull : kRowWhole);
+    s.block = kWave * s.wpt;
+    s.grid = T;
+    s.nr = 1;
+    s.lds = token_sum_lds_bytes(s.wpt, 1);
+    return s;
+}
+
+bool uses_wide_kernel(int64_t T, int32_t H, int32_t k, bool per_expert) {
+    if (per_expert || k != kCompiledTopK || row_shape(1, H, kMaxWaves, kMaxVpl).vpl <= 2) return false;
+    const RowShape s = wide_shape(T, H);
+    return s.tail == kRowFull && s.vpl >= 3 && s.vpl <= kWideMaxVpl;
+}
+
+// Launch shape of the finalize kernels; `wide` selects the slot-serial kernel's (the bf16-output
+// finalize of wide rows only).
+RowShape finalize_shape(int64_t T, int32_t H, int32_t k, bool per_expert, bool wide = false) {
+    if (wide) return wide_shape(T, H);
     RowShape s = per_expert ? row_shape(T, H, kMaxWavesPerExpert, kMaxVplPerExpert)
                             : row_shape(T, H, kMaxWaves, kMaxVpl);
     const int kc = k == kCompiledTopK && uses_compiled_topk(s.vpl, per_expert) ? kCompiledTopK : 0;
@@ -90,7 +120,20 @@ const void* finalize_kernel_for_mode(const RowShape& s, int k, bool per_expert) 
     }
 }
 
-const void* finalize_kernel_for(const RowShape& s, int k, bool per_expert, bool partial = false) {
+const void* wide_kernel_for(const RowShape& s) {
+    switch (s.vpl) {
+        case 3: return reinterpret_cast<const void*>(&moe_finalize_wide_kernel<3, kCompiledTopK>);
+        case 4: return reinterpret_cast<const void*>(&moe_finalize_wide_kernel<4, kCompiledTopK>);
+        case 5: return reinterpret_cast<const void*>(&moe_finalize_wide_kernel<5, kCompiledTopK>);
+        default: return nullptr;
+    }
+}
+
+// The finalize kernel for a shape (wide: the slot-serial kernel of wide rows), or its
+// expert-parallel partial.
+const void* finalize_kernel_for(const RowShape& s, int k, bool per_expert, bool partial = false,
+                                bool wide = false) {
+    if (wide) return wide_kernel_for(s);
     return partial ? finalize_kernel_for_mode<true>(s, k, per_expert)
                    : finalize_kernel_for_mode<false>(s, k, per_expert);
 }
@@ -149,12 +192,13 @@ int mf_launch_shape(int kind, int64_t T, int32_t H, int32_t k, int32_t* waves_pe
     if (kind < 0 || kind > 3 || T < 0) return MF_ERR_SHAPE;
     if (kind <= 1 ? !mf_moe_finalize_supported(H, k, kind) : !row_width_supported(H))
         return MF_ERR_UNSUPPORTED;
-    const RowShape s = kind <= 1   ? finalize_shape(T, H, k, kind == 1)
+    const bool wide = kind <= 1 && uses_wide_kernel(T, H, k, kind == 1);
+    const RowShape s = kind <= 1   ? finalize_shape(T, H, k, kind == 1, wide)
                        : kind == 2 ? row_shape(T, H, kMaxWaves, kMaxVpl)
                                    : combine_shape(T, H);
     if (T > 0 && !grid_fits(s.grid, s.block)) return MF_ERR_SHAPE;
     // the same kernel lookup as the launch itself
-    const void* fn = kind <= 1   ? finalize_kernel_for(s, k, kind == 1)
+    const void* fn = kind <= 1   ? finalize_kernel_for(s, k, kind == 1, false, wide)
                      : kind == 2 ? gated_kernel_for(s, false)
                                  : combine_kernel_for(s);
     if (!fn || (kind <= 1 && s.block > finalize_block_max(kind == 1))) return MF_ERR_UNSUPPORTED;
@@ -174,9 +218,10 @@ int mf_moe_finalize(const uint16_t* expert_rows, int64_t num_rows, const int32_t
     const bool per_expert = expert_ids != nullptr || expert_gamma != nullptr;
     if (!mf_moe_finalize_supported(H, k, per_expert)) return MF_ERR_UNSUPPORTED;
     if (T == 0) return MF_OK;
-    const RowShape s = finalize_shape(T, H, k, per_expert);
+    const bool wide = uses_wide_kernel(T, H, k, per_expert);
+    const RowShape s = finalize_shape(T, H, k, per_expert, wide);
     if (!grid_fits(s.grid, s.block)) return MF_ERR_SHAPE;
-    const void* fn = finalize_kernel_for(s, k, per_expert);
+    const void* fn = finalize_kernel_for(s, k, per_expert, false, wide);
     if (!fn || s.block > finalize_block_max(per_expert)) return MF_ERR_UNSUPPORTED;
     if (!expert_rows || !idx || !weights || !residual || !residual_out || !gamma || !out)
         return MF_ERR_NULL;

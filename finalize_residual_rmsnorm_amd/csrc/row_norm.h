@@ -148,39 +148,44 @@ __device__ __forceinline__ float lane_sumsq(const float (&r)[VPL][8], const Slot
 // row the kernels write (the residual, the expert-parallel partial).  Measured: the finalize
 // 1.5% and the gated-residual norm 7% faster than the direct stores, results identical.
 // (The slots argument only selects the tail handling.)
-template <int VPL, int TAIL>
-__device__ __forceinline__ void store_residual(const float (&r)[VPL][8], const Slots<VPL, TAIL>&,
-                                               const RowMap& m, int H, float* row) {
+// One slot (the 512 values from slot * 512) of the row, held as 8 values per lane.
+template <int TAIL>
+__device__ __forceinline__ void store_residual_slot(const float (&v)[8], int slot, const RowMap& m,
+                                                    int H, float* row) {
     const int l = m.lane;
     const int a0 = (l >> 1) << 2, a1 = (32 + (l >> 1)) << 2;  // source lanes, as byte addresses
     const bool odd = l & 1;
+    const uint32_t base = uint32_t(slot * kSlot);
+    float t0[4], t1[4];
 #pragma unroll
-    for (int s = 0; s < VPL; ++s) {
-        const uint32_t base = uint32_t((m.wave * VPL + s) * kSlot);
-        float t0[4], t1[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int lo = __float_as_int(r[s][i]), hi = __float_as_int(r[s][4 + i]);
-            const float x0 = __int_as_float(__builtin_amdgcn_ds_bpermute(a0, lo));
-            const float y0 = __int_as_float(__builtin_amdgcn_ds_bpermute(a0, hi));
-            const float x1 = __int_as_float(__builtin_amdgcn_ds_bpermute(a1, lo));
-            const float y1 = __int_as_float(__builtin_amdgcn_ds_bpermute(a1, hi));
-            t0[i] = odd ? y0 : x0;
-            t1[i] = odd ? y1 : x1;
-        }
-        const uint32_t e0 = base + 4u * l, e1 = base + 256u + 4u * l;
-        bool v0, v1;
-        if constexpr (TAIL == kRowFull) {
-            v0 = v1 = true;
-        } else if constexpr (TAIL == kRowWhole) {
-            v0 = v1 = base < uint32_t(H);
-        } else {
-            v0 = e0 < uint32_t(H);
-            v1 = e1 < uint32_t(H);
-        }
-        if (v0) st_stream(f32x4{t0[0], t0[1], t0[2], t0[3]}, at<f32x4>(row, e0 * 4u));
-        if (v1) st_stream(f32x4{t1[0], t1[1], t1[2], t1[3]}, at<f32x4>(row, e1 * 4u));
+    for (int i = 0; i < 4; ++i) {
+        const int lo = __float_as_int(v[i]), hi = __float_as_int(v[4 + i]);
+        const float x0 = __int_as_float(__builtin_amdgcn_ds_bpermute(a0, lo));
+        const float y0 = __int_as_float(__builtin_amdgcn_ds_bpermute(a0, hi));
+        const float x1 = __int_as_float(__builtin_amdgcn_ds_bpermute(a1, lo));
+        const float y1 = __int_as_float(__builtin_amdgcn_ds_bpermute(a1, hi));
+        t0[i] = odd ? y0 : x0;
+        t1[i] = odd ? y1 : x1;
     }
+    const uint32_t e0 = base + 4u * l, e1 = base + 256u + 4u * l;
+    bool v0, v1;
+    if constexpr (TAIL == kRowFull) {
+        v0 = v1 = true;
+    } else if constexpr (TAIL == kRowWhole) {
+        v0 = v1 = base < uint32_t(H);
+    } else {
+        v0 = e0 < uint32_t(H);
+        v1 = e1 < uint32_t(H);
+    }
+    if (v0) st_stream(f32x4{t0[0], t0[1], t0[2], t0[3]}, at<f32x4>(row, e0 * 4u));
+    if (v1) st_stream(f32x4{t1[0], t1[1], t1[2], t1[3]}, at<f32x4>(row, e1 * 4u));
+}
+
+template <int VPL, int TAIL>
+__device__ __forceinline__ void store_residual(const float (&r)[VPL][8], const Slots<VPL, TAIL>&,
+                                               const RowMap& m, int H, float* row) {
+#pragma unroll
+    for (int s = 0; s < VPL; ++s) store_residual_slot<TAIL>(r[s], m.wave * VPL + s, m, H, row);
 }
 
 // gamma slice of the lane (bf16, loaded early so that its latency overlaps other work).
@@ -197,11 +202,14 @@ __device__ __forceinline__ void load_gamma(u32x4 (&g)[VPL], const uint16_t* gamm
 // the finalize and the gated-residual norm are faster with the default policy (4% for the
 // finalize; each wave instruction writes whole 128-byte lines), the expert-parallel combine
 // 3% faster with nontemporal stores.
+// (lane_ss: the lane's sum of squares of its valid values, its slots in order, if the caller
+// has already formed it as lane_sumsq would; else it is formed here.)
 template <bool OUT_NT = false, int VPL, int TAIL>
 __device__ __forceinline__ void rmsnorm_store(const float (&r)[VPL][8], const u32x4 (&g)[VPL],
                                               const Slots<VPL, TAIL>& sl, uint16_t* out_row,
-                                              int H, float eps, TokenLds& L, const RowMap& m) {
-    float ss[1] = {lane_sumsq(r, sl)};
+                                              int H, float eps, TokenLds& L, const RowMap& m,
+                                              const float* lane_ss = nullptr) {
+    float ss[1] = {lane_ss ? *lane_ss : lane_sumsq(r, sl)};
     token_sum<1>(ss, L, m);
     const float inv = rms_scale(ss[0], 1.0f / (float)H, eps);
 #pragma unroll

@@ -80,7 +80,8 @@ def test_named_finalize_workloads_follow_the_logits_recipe():
     import workloads
     for name in ("finalize_tiny", "finalize_decode_per_expert", "finalize_prefill",
                  "finalize_1tok", "finalize_1tok_per_expert", "finalize_ep_partial",
-                 "finalize_prefill_mxfp4"):
+                 "finalize_prefill_mxfp4", "finalize_wide_12288", "finalize_wide_20480",
+                 "finalize_wide_32768"):
         assert workloads.WORKLOADS[name]["routing"] == "logits", name
     assert workloads.WORKLOADS["finalize_tiny"]["layout"] == "random"
     assert workloads.WORKLOADS["finalize_prefill"]["layout"] == "expert_sorted"

@@ -133,6 +133,11 @@ FINALIZE_SHAPES = [
     (9, 776, 4, "random"), (65, 5000, 8, "expert_grouped"),
     # a grid past 65535 workgroups
     (70000, 64, 2, "random"),
+    # wide rows at the compiled top-8 (the slot-serial kernel): whole waves of slots (12288,
+    # 20480, 32768), a spare slot in a live wave (9216, 12800) and a last slot cut inside (12296)
+    (600, 12288, 8, "expert_grouped"), (257, 20480, 8, "random"), (130, 32768, 8, "random"),
+    (9, 9216, 8, "random"), (5, 12800, 8, "random"), (7, 12296, 8, "random"),
+    (3, 16384, 8, "random"), (11, 24576, 8, "random"),
 ]
 
 

@@ -92,6 +92,17 @@ WORKLOADS = {
     "finalize_1tok_per_expert": dict(kind="finalize", T=1, H=4096, E=128, k=8, seed=13,
                                      routing="logits", layout="expert_sorted", per_expert=True,
                                      residual_std=2.0),
+    # Wide rows (hidden sizes past 8192) at top-8, the prefill recipe with fewer tokens: each
+    # still moves 2.2-3.5 GB, far past the Infinity Cache.
+    "finalize_wide_12288": dict(kind="finalize", T=8192, H=12288, E=256, k=8, seed=14,
+                                routing="logits", layout="expert_sorted", per_expert=False,
+                                residual_std=1.0),
+    "finalize_wide_20480": dict(kind="finalize", T=4096, H=20480, E=256, k=8, seed=15,
+                                routing="logits", layout="expert_sorted", per_expert=False,
+                                residual_std=1.0),
+    "finalize_wide_32768": dict(kind="finalize", T=4096, H=32768, E=256, k=8, seed=16,
+                                routing="logits", layout="expert_sorted", per_expert=False,
+                                residual_std=1.0),
     # Expert parallelism over 8 GPUs at the prefill size: this GPU's partial (its 32 of the 256
     # experts; the other slots are marked -1) and the owner's combine of 8 partials for its
     # 2048 tokens.
