@@ -74,6 +74,7 @@ KERNEL_SOURCES = {
     "gated_next": _NORM_SOURCES,
     "per_head": _NORM_SOURCES,
     "copy": _NORM_SOURCES,
+    "empty_grid": _NORM_SOURCES,
     "route": ["mf_device.h", "route_kernels.h", "api_util.h", "route_api.hip"],
     "rmsnorm_mx": ["mf_device.h", "row_norm.h", "mx_device.h", "mx_kernels.h", "api_util.h",
                    "row_shape.h", "mx_api.hip"],
