@@ -123,3 +123,54 @@ def test_graph_replays_match_eager():
     torch.cuda.synchronize()
     bad = same(snapshot(o2), snapshot(o))
     assert bad is None, f"replay with new inputs: {bad} differs from the eager result"
+
+
+def test_graph_wide_per_expert_and_noalloc_route():
+    """A second captured graph with this library's other launch paths: the slot-serial finalize of
+    wide rows (H=12288, k=8), the per-expert finalize, and the routing call on the library's static
+    scratch (the allocation-free form made for captured graphs: it looks up its scratch on the
+    first, eager, call and allocates nothing).  Replayed three times with eager work between;
+    every replay matches the eager results bit for bit."""
+    say("graph 2: wide finalize T=40 H=12288 k=8, per-expert finalize T=33 H=4096 k=8, "
+        "route_noalloc T=300 E=256 k=8")
+    f = workloads.make_finalize_inputs(40, 12288, E=64, k=8, seed=71)
+    p = workloads.make_finalize_inputs(33, 4096, E=32, k=8, seed=72, per_expert=True)
+    r = workloads.make_route_inputs(300, 256, 8, seed=73)
+    src = dict(rows=up(f["expert_rows"], True), idx=up(f["idx"]), w=up(f["weights"]),
+               res=up(f["residual"]), gamma=up(f["gamma"], True),
+               prows=up(p["expert_rows"], True), pidx=up(p["idx"]), pw=up(p["weights"]),
+               pres=up(p["residual"]), pgamma=up(p["gamma"], True), peids=up(p["expert_ids"]),
+               pegamma=up(p["expert_gamma"], True), logits=up(r["logits"]))
+    e = lambda shape, dt: torch.empty(shape, dtype=dt, device=DEV)
+    o = dict(r=e((40, 12288), torch.float32), out=e((40, 12288), torch.bfloat16),
+             pr=e((33, 4096), torch.float32), pout=e((33, 4096), torch.bfloat16),
+             eids=e((300, 8), torch.int32), ew=e((300, 8), torch.float32),
+             ridx=e((300, 8), torch.int32), perm=e((2400,), torch.int32), offs=e((257,), torch.int32))
+
+    def launch():
+        mf.mf_moe_finalize(src["rows"], src["idx"], src["w"], src["res"], src["gamma"], 1e-6,
+                           residual_out=o["r"], out=o["out"])
+        mf.mf_moe_finalize(src["prows"], src["pidx"], src["pw"], src["pres"], src["pgamma"], 1e-6,
+                           expert_ids=src["peids"], expert_gamma=src["pegamma"],
+                           residual_out=o["pr"], out=o["pout"])
+        mf.mf_moe_route_noalloc(src["logits"], 8, expert_ids=o["eids"], weights=o["ew"],
+                                idx=o["ridx"], perm=o["perm"], offsets=o["offs"])
+
+    assert mf.mf_launch_shape(0, 40, 12288, 8)["vectors_per_lane"] == 3   # the wide kernel's shape
+    launch()
+    torch.cuda.synchronize()
+    eager = snapshot(o)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for v in o.values():
+            v.zero_()
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        bad = same(eager, snapshot(o))
+        assert bad is None, f"replay {rep}: {bad} differs from the eager result"
+        assert torch.isfinite(junk)

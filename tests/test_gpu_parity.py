@@ -224,6 +224,32 @@ def test_finalize_on_a_side_stream():
     assert_bf16_close(bits(out), o_ref)
 
 
+def test_finalize_on_concurrent_streams():
+    # the library keeps no state between calls: two streams running different problems at once
+    # each get their own results (the same bits as run alone)
+    a = workloads.make_finalize_inputs(700, 7168, E=64, k=8, seed=86)
+    b = workloads.make_finalize_inputs(300, 12288, E=64, k=8, seed=87)
+    say("concurrent streams: T=700 H=7168 and T=300 H=12288, k=8")
+    alone_a = finalize_gpu(a)
+    alone_b = finalize_gpu(b)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)
+    ins_a = (up(a["expert_rows"], True), up(a["idx"]), up(a["weights"]), up(a["residual"]),
+             up(a["gamma"], True), a["eps"])
+    ins_b = (up(b["expert_rows"], True), up(b["idx"]), up(b["weights"]), up(b["residual"]),
+             up(b["gamma"], True), b["eps"])
+    torch.cuda.synchronize()
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            oa, ra = mf.mf_moe_finalize(*ins_a)
+        with torch.cuda.stream(s2):
+            ob, rb = mf.mf_moe_finalize(*ins_b)
+        s1.synchronize()
+        s2.synchronize()
+        assert torch.equal(ra, alone_a[1]) and torch.equal(oa.view(torch.int16), alone_a[0].view(torch.int16))
+        assert torch.equal(rb, alone_b[1]) and torch.equal(ob.view(torch.int16), alone_b[0].view(torch.int16))
+
+
 def test_zero_tokens_is_a_no_op():
     d = workloads.make_finalize_inputs(1, 64, E=4, k=2, seed=80)
     rows = up(d["expert_rows"], True)
