@@ -19,7 +19,8 @@
  *  - Tensors are dense and row-major.  bfloat16 data is passed as raw 16-bit patterns
  *    (uint16_t).  All tensor pointers are device pointers on the current HIP device.
  *  - The caller owns every buffer.  The library allocates nothing, keeps no state between
- *    calls and is safe to call from several threads.
+ *    calls and is safe to call from several threads (mf_moe_route_noalloc alone keeps a static
+ *    per-GPU scratch array; see its declaration).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the null stream).
  *    The library never synchronizes.
  *  - Arguments are checked on the host before any HIP call.  On a failed check the function

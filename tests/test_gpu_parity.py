@@ -195,6 +195,24 @@ def test_finalize_batch_invariance():
     assert torch.equal(out_big[:5].view(torch.int16), out_small.view(torch.int16))
 
 
+@pytest.mark.parametrize("H", [12288, 20480, 32768])
+def test_wide_finalize_batch_invariance_and_in_place(H):
+    # the slot-serial kernel of wide rows: a token's bits do not depend on the batch, and the
+    # in-place update of the residual stream gives the same bits as a separate output
+    d = workloads.make_finalize_inputs(300, H, E=64, k=8, seed=88 + H)
+    say(f"wide batch invariance / in place H={H}: {shape_str(0, 300, H, 8)}")
+    out_big, r_big = finalize_gpu(d)
+    small = dict(d, T=3, idx=d["idx"][-3:], weights=d["weights"][-3:], residual=d["residual"][-3:])
+    out_small, r_small = finalize_gpu(small)
+    res = up(d["residual"])
+    out_ip, _ = mf.mf_moe_finalize(up(d["expert_rows"], True), up(d["idx"]), up(d["weights"]), res,
+                                   up(d["gamma"], True), d["eps"], residual_out=res)
+    torch.cuda.synchronize()
+    assert torch.equal(r_big[-3:], r_small)
+    assert torch.equal(out_big[-3:].view(torch.int16), out_small.view(torch.int16))
+    assert torch.equal(res, r_big) and torch.equal(out_ip.view(torch.int16), out_big.view(torch.int16))
+
+
 def test_finalize_guard_bands():
     T, H, k = 37, 520, 3
     say(f"guard bands T={T} H={H} k={k}: {shape_str(0, T, H, k)}")
