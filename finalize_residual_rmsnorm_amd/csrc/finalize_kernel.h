@@ -76,6 +76,16 @@ constexpr int finalize_min_waves(int vpl, bool per_expert) {
     return per_expert ? 2 : (vpl == 1 ? 8 : 4);
 }
 
+// The slot-serial kernel of wide rows: 8 waves per token, NL of each wave's VPL slots staged in
+// LDS after the reduction area (16-byte aligned).
+constexpr int kWideWaves = 8;
+__host__ __device__ constexpr int wide_stage_offset(int wpt) {
+    return (int(token_sum_lds_bytes(wpt, 1) / sizeof(float)) + 3) & ~3;
+}
+constexpr size_t wide_lds_bytes(int wpt, int nl) {
+    return size_t(wide_stage_offset(wpt)) * sizeof(float) + size_t(wpt) * nl * kSlot * sizeof(float);
+}
+
 // One gather batch: JB rows (and, per-expert, their gamma rows) of the lane's slots; with
 // SKIP, which of them are local (live).
 template <int VPL, int JB, bool PER_EXPERT, bool SKIP = false>
@@ -264,20 +274,38 @@ moe_finalize_kernel(const FinalizeArgs a) {
 // Wide rows (several 512-value slots per wave, compile-time top-k of at most 8): the same
 // arithmetic as moe_finalize_kernel, with the gather run slot by slot.  A slot's k rows and its
 // residual are loaded together, and the next slot's are issued before this slot's are summed, so
-// two slots' rows are in flight while only the finished fp32 values of earlier slots wait in
-// registers for the norm.  (moe_finalize_kernel holds every slot's rows of a batch at once,
-// which leaves room for two rows per slot at three or four slots per wave.)  Per slot the rows
-// are summed in ascending j exactly as there: the results are bit-identical to it.
-// Measured on MI355X (T = 4096-8192, k = 8, cold inputs): H = 20480 at 8 waves of 5 slots 74.5% of
-// 8 TB/s (72.4% before), H = 32768 at 16 waves of 4 slots 72.5-73.0% (70.3-70.6%), H = 12288 at
-// 8 waves of 3 slots 77.3% (77.6%).  Not taken: 4-row batches with a 64-VGPR cap for two
-// workgroups per CU (spills; 34-62%), per-slot residual stores (1-3% slower), and a persistent
-// form whose lookahead crosses into the next token (spills at every width).
-template <int VPL, int KC>
-__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 8)))
+// two slots' rows are in flight while only the finished fp32 values of earlier slots wait for
+// the norm.  Per slot the rows are summed in ascending j and the lane's sum of squares runs over
+// its slots in order, exactly as there: on the same launch shape the results are bit-identical to
+// it.  Measured on MI355X at 3 and 5 slots (8 waves, T = 4096-8192, k = 8, cold): H = 12288 77.3%
+// of 8 TB/s (77.6% for moe_finalize_kernel), H = 20480 74.5% (72.4%).  Not taken: 4-row batches
+// with a 64-VGPR cap for two 16-wave workgroups per CU (spills; 34-62%), per-slot residual stores
+// (1-3% slower), and a persistent form whose lookahead crosses into the next token (spills at
+// every width).
+//
+// The finished fp32 row waits in registers for the norm: 8 values per slot and lane, 64 at
+// H = 32768 with 8 waves, more than the registers of two workgroups per CU allow.  So the first NL
+// slots of each wave wait in LDS instead (2 KiB per slot and wave, lane-major: each 16-byte access
+// of a wave is 1 KiB contiguous, free of bank conflicts) and are read back for the residual store
+// and the norm; only the last VPL - NL stay in VGPRs.  At 6 to 8 slots per wave three are staged
+// (52 KiB per workgroup): two 8-wave workgroups per CU, no spills.
+// Measured on MI355X (T = 4096, k = 8, cold, same box, interleaved runs):
+//  - H = 32768: 72.6-73.0% of 8 TB/s against 72.2-72.8% for 16 waves of 4 slots in registers;
+//    H = 28672: 72.6-72.8% against 72.2% for moe_finalize_kernel.
+//  - Not taken: staging at 5 slots for three workgroups per CU at H = 20480 (70.6% against 74.7%),
+//    one staged slot at H = 12288 (71.9% against 77.2%): capped at 80 VGPRs, the waves keep fewer
+//    loads in flight.  Slots interleaved across waves (s * 8 + w, so that the workgroup reads 8 KiB
+//    of each row contiguously at each step): 70.5% at H = 32768.  The residual's loads issued
+//    ahead of the rows': within 0.5% either way.
+//
+// Every residual load of the token precedes its residual_out stores: the in-place case is safe.
+template <int VPL, int NL, int KC>
+__global__ void __launch_bounds__(kWideWaves * kWave) __attribute__((amdgpu_waves_per_eu(4, 8)))
 moe_finalize_wide_kernel(const FinalizeArgs a) {
     static_assert(KC > 0 && KC <= 8, "one batch of rows per slot");
+    static_assert(NL >= 0 && NL < VPL, "at least one slot stays in registers");
     constexpr int TAIL = kRowFull;
+    constexpr int NREG = VPL - NL;
     extern __shared__ float lds[];
     const RowMap m = row_map();
     const int H = a.H;
@@ -285,6 +313,9 @@ moe_finalize_wide_kernel(const FinalizeArgs a) {
     const int64_t tk = m.t * KC;
     const float* res = a.residual + m.t * H;
     TokenLds L = token_lds(lds, m.wpt, 1);
+    // this lane's staged values: slot s, half h at stage[(s * 2 + h) * 64]
+    f32x4* stage = reinterpret_cast<f32x4*>(lds + wide_stage_offset(m.wpt)) +
+                   m.wave * NL * 2 * kWave + m.lane;
 
     auto slot_of = [&](int s) {
         Slots<1, TAIL> one;
@@ -293,7 +324,16 @@ moe_finalize_wide_kernel(const FinalizeArgs a) {
         one.suni[0] = sl.suni[s];
         return one;
     };
-    float r[VPL][8];
+    auto staged = [&](int s, float (&v)[8]) {
+        const f32x4 lo = stage[(s * 2) * kWave], hi = stage[(s * 2 + 1) * kWave];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = lo[i];
+            v[4 + i] = hi[i];
+        }
+    };
+    float r[NREG][8];
+    float lane_ss = 0.0f;   // the lane's sum of squares, its slots in order
     f32x4 rv[2][2];
     GatherBatch<1, KC, false> b[2];
     auto issue = [&](int buf, int s) {
@@ -309,17 +349,51 @@ moe_finalize_wide_kernel(const FinalizeArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[0][i] = 0.0f;
         consume_batch(b[s & 1], acc, a, tk, 0, KC, slot_of(s), L, m);
+        float v[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            r[s][i] = rv[s & 1][0][i] + acc[0][i];
-            r[s][4 + i] = rv[s & 1][1][i] + acc[0][4 + i];
+            v[i] = rv[s & 1][0][i] + acc[0][i];
+            v[4 + i] = rv[s & 1][1][i] + acc[0][4 + i];
+        }
+        if (s < NL) {
+            lane_ss += sumsq8(v);
+            stage[(s * 2) * kWave] = f32x4{v[0], v[1], v[2], v[3]};
+            stage[(s * 2 + 1) * kWave] = f32x4{v[4], v[5], v[6], v[7]};
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) r[s - NL][i] = v[i];
         }
     }
     u32x4 g[VPL];
     load_gamma(g, a.gamma, sl);
-    // every residual load precedes every residual_out store: the in-place case is safe
-    store_residual(r, sl, m, H, a.residual_out + m.t * H);
-    rmsnorm_store(r, g, sl, a.out + m.t * H, H, a.eps, L, m);
+    float* res_out = a.residual_out + m.t * H;
+#pragma unroll
+    for (int s = 0; s < VPL; ++s) {
+        if (s < NL) {
+            float v[8];
+            staged(s, v);
+            store_residual_slot<TAIL>(v, m.wave * VPL + s, m, H, res_out);
+        } else {
+            store_residual_slot<TAIL>(r[s - NL], m.wave * VPL + s, m, H, res_out);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < NREG; ++s) lane_ss += sumsq8(r[s]);
+    float ss[1] = {lane_ss};
+    token_sum<1>(ss, L, m);
+    const float inv = rms_scale(ss[0], 1.0f / (float)H, a.eps);
+    uint16_t* out_row = a.out + m.t * H;
+#pragma unroll
+    for (int s = 0; s < VPL; ++s) {
+        uint16_t* dst = at<uint16_t>(out_row, sl.eoff[s] * 2u);
+        if (s < NL) {
+            float v[8];
+            staged(s, v);
+            norm_store_slot(v, g[s], inv, dst);
+        } else {
+            norm_store_slot(r[s - NL], g[s], inv, dst);
+        }
+    }
 }
 
 // The token owner's combine of the expert-parallel split.

@@ -37,22 +37,24 @@ RowShape combine_shape(int64_t T, int32_t H) {
 
 // Rows too wide for one or two slots per wave (H > 8192) take the slot-serial kernel
 // (moe_finalize_wide_kernel) at the compiled top-k when its shape fills whole waves of slots:
-// 8 waves per token up to 40 slots (H <= 20480), 16 beyond, measured fastest at H = 12288, 20480
-// and 32768.  Other wide shapes (a row that is not whole waves of whole slots, another top-k)
-// keep moe_finalize_kernel.
-constexpr int kWideMaxVpl = 5;
+// 8 waves per token of 3 or 5 to 8 slots each (H = 12288, 20480, 24576, 28672, 32768; at
+// H = 16384 two slots per wave of 16 waves fit in registers), of which wide_staged_slots wait
+// in LDS.  Other wide shapes (a row that is not whole waves of whole
+// slots, another top-k) keep moe_finalize_kernel.
+constexpr int kWideMaxVpl = 8;
+constexpr int wide_staged_slots(int vpl) { return vpl >= 6 ? 3 : 0; }
 
 RowShape wide_shape(int64_t T, int32_t H) {
     const int ns = (H + kSlot - 1) / kSlot;
-    const int waves = ns <= 40 ? 8 : 16;
     RowShape s;
-    s.vpl = (ns + waves - 1) / waves;
-    s.wpt = pow2_at_least((ns + s.vpl - 1) / s.vpl);
-    s.tail = H != ns * kSlot ? kRowRagged : (ns == s.wpt * s.vpl ? kRowFull : kRowWhole);
+    s.vpl = (ns + kWideWaves - 1) / kWideWaves;
+    s.wpt = kWideWaves;
+    s.tail = ns == s.wpt * s.vpl && H == ns * kSlot ? kRowFull : kRowWhole;
     s.block = kWave * s.wpt;
     s.grid = T;
     s.nr = 1;
-    s.lds = token_sum_lds_bytes(s.wpt, 1);
+    s.nl = wide_staged_slots(s.vpl);
+    s.lds = wide_lds_bytes(s.wpt, s.nl);
     return s;
 }
 
@@ -120,11 +122,19 @@ const void* finalize_kernel_for_mode(const RowShape& s, int k, bool per_expert) 
     }
 }
 
+template <int VPL>
+const void* wide_fn() {
+    return reinterpret_cast<const void*>(
+        &moe_finalize_wide_kernel<VPL, wide_staged_slots(VPL), kCompiledTopK>);
+}
+
 const void* wide_kernel_for(const RowShape& s) {
     switch (s.vpl) {
-        case 3: return reinterpret_cast<const void*>(&moe_finalize_wide_kernel<3, kCompiledTopK>);
-        case 4: return reinterpret_cast<const void*>(&moe_finalize_wide_kernel<4, kCompiledTopK>);
-        case 5: return reinterpret_cast<const void*>(&moe_finalize_wide_kernel<5, kCompiledTopK>);
+        case 3: return wide_fn<3>();
+        case 5: return wide_fn<5>();
+        case 6: return wide_fn<6>();
+        case 7: return wide_fn<7>();
+        case 8: return wide_fn<8>();
         default: return nullptr;
     }
 }

@@ -204,6 +204,22 @@ __device__ __forceinline__ void load_gamma(u32x4 (&g)[VPL], const uint16_t* gamm
 // 3% faster with nontemporal stores.
 // (lane_ss: the lane's sum of squares of its valid values, its slots in order, if the caller
 // has already formed it as lane_sumsq would; else it is formed here.)
+// The bf16 out of one slot's 8 values of a lane: bf16((v * inv) * gamma), stored at dst.
+template <bool OUT_NT = false>
+__device__ __forceinline__ void norm_store_slot(const float (&v)[8], const u32x4& g, float inv,
+                                                uint16_t* dst) {
+    float gf[8];
+    widen8(g, gf);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = pack_bf16x2((v[2 * i] * inv) * gf[2 * i], (v[2 * i + 1] * inv) * gf[2 * i + 1]);
+    if constexpr (OUT_NT)
+        st_stream(o, reinterpret_cast<u32x4*>(dst));
+    else
+        *reinterpret_cast<u32x4*>(dst) = o;
+}
+
 template <bool OUT_NT = false, int VPL, int TAIL>
 __device__ __forceinline__ void rmsnorm_store(const float (&r)[VPL][8], const u32x4 (&g)[VPL],
                                               const Slots<VPL, TAIL>& sl, uint16_t* out_row,
@@ -213,21 +229,8 @@ __device__ __forceinline__ void rmsnorm_store(const float (&r)[VPL][8], const u3
     token_sum<1>(ss, L, m);
     const float inv = rms_scale(ss[0], 1.0f / (float)H, eps);
 #pragma unroll
-    for (int s = 0; s < VPL; ++s) {
-        float gf[8];
-        widen8(g[s], gf);
-        u32x4 o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            o[i] = pack_bf16x2((r[s][2 * i] * inv) * gf[2 * i],
-                               (r[s][2 * i + 1] * inv) * gf[2 * i + 1]);
-        if (sl.sval[s]) {
-            if constexpr (OUT_NT)
-                st_stream(o, at<u32x4>(out_row, sl.eoff[s] * 2u));
-            else
-                *at<u32x4>(out_row, sl.eoff[s] * 2u) = o;
-        }
-    }
+    for (int s = 0; s < VPL; ++s)
+        if (sl.sval[s]) norm_store_slot<OUT_NT>(r[s], g[s], inv, at<uint16_t>(out_row, sl.eoff[s] * 2u));
 }
 
 }  // namespace mf

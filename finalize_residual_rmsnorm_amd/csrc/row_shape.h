@@ -28,6 +28,7 @@ struct RowShape {
     int block;      // threads per workgroup
     int64_t grid;   // workgroups = tokens
     int nr;         // row sums per reduction barrier
+    int nl = 0;     // slots per wave staged in LDS (the slot-serial kernel of wide rows)
     size_t lds;     // dynamic LDS bytes
 };
 

@@ -266,8 +266,15 @@ def test_launch_shapes():
     # 12288 = 24 slots: 8 waves of 3 leave no spare slot (16 waves of 2 would leave 8)
     assert mf.mf_launch_shape(mf.KIND_FINALIZE, 5, 12288, 8) == dict(
         waves_per_token=8, vectors_per_lane=3, block=512, grid=5)
-    # the widest row: 64 slots over 16 waves
-    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 100000, 32768, 8)["vectors_per_lane"] == 4
+    # the widest row: 64 slots; at the compiled top-8 the slot-serial kernel's 8 waves of 8 slots
+    # (three of them staged in LDS), at another k 16 waves of 4
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 100000, 32768, 8) == dict(
+        waves_per_token=8, vectors_per_lane=8, block=512, grid=100000)
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 7, 32768, 6) == dict(
+        waves_per_token=16, vectors_per_lane=4, block=1024, grid=7)
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 7, 20480, 8)["vectors_per_lane"] == 5
+    # whole waves of whole slots only: 13312 = 26 slots keeps the batched kernel
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 7, 13312, 8)["waves_per_token"] == 16
     # the EP combine runs at most 8 waves per token, 16 when 8 waves of 4 slots cannot hold the row
     assert mf.mf_launch_shape(mf.KIND_EP_COMBINE, 2048, 7168) == dict(
         waves_per_token=8, vectors_per_lane=2, block=512, grid=2048)

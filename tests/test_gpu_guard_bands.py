@@ -68,7 +68,9 @@ def check_all(g, expected):
 
 
 @pytest.mark.parametrize("T,H,k,pe", [(37, 520, 3, False), (9, 776, 8, False), (5, 4128, 8, False),
-                                      (3, 7168, 8, True), (11, 520, 5, True)])
+                                      (3, 7168, 8, True), (11, 520, 5, True),
+                                      # wide rows: the slot-serial kernel with slots staged in LDS
+                                      (3, 20480, 8, False), (2, 32768, 8, False)])
 def test_finalize_guard_bands(T, H, k, pe):
     say(f"guard bands finalize T={T} H={H} k={k} per_expert={pe}")
     d = workloads.make_finalize_inputs(T, H, E=16, k=k, seed=1100 + T + H + k, per_expert=pe,

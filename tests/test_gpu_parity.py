@@ -133,11 +133,12 @@ FINALIZE_SHAPES = [
     (9, 776, 4, "random"), (65, 5000, 8, "expert_grouped"),
     # a grid past 65535 workgroups
     (70000, 64, 2, "random"),
-    # wide rows at the compiled top-8 (the slot-serial kernel): whole waves of slots (12288,
-    # 20480, 32768), a spare slot in a live wave (9216, 12800) and a last slot cut inside (12296)
+    # wide rows at the compiled top-8 (the slot-serial kernel, 8 waves of 3 and of 5 to 8 slots,
+    # up to three of them staged in LDS): whole waves of slots (12288, 20480, 24576, 28672,
+    # 32768), a spare slot in a live wave (9216, 12800) and a last slot cut inside (12296)
     (600, 12288, 8, "expert_grouped"), (257, 20480, 8, "random"), (130, 32768, 8, "random"),
     (9, 9216, 8, "random"), (5, 12800, 8, "random"), (7, 12296, 8, "random"),
-    (3, 16384, 8, "random"), (11, 24576, 8, "random"),
+    (3, 16384, 8, "random"), (11, 24576, 8, "random"), (13, 28672, 8, "random"),
 ]
 
 
@@ -195,7 +196,7 @@ def test_finalize_batch_invariance():
     assert torch.equal(out_big[:5].view(torch.int16), out_small.view(torch.int16))
 
 
-@pytest.mark.parametrize("H", [12288, 20480, 32768])
+@pytest.mark.parametrize("H", [12288, 20480, 24576, 28672, 32768])
 def test_wide_finalize_batch_invariance_and_in_place(H):
     # the slot-serial kernel of wide rows: a token's bits do not depend on the batch, and the
     # in-place update of the residual stream gives the same bits as a separate output
