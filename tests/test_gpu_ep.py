@@ -82,6 +82,10 @@ def per_expert_bound(d, idx):
     (17, 1024, 8, 2, False), (33, 4104, 9, 3, False), (100, 7168, 8, 8, False),
     (5, 32768, 3, 2, False), (64, 4096, 8, 4, True), (9, 520, 5, 2, True), (300, 2048, 1, 4, False),
     (9, 776, 5, 2, False), (6, 5000, 8, 3, True),
+    # the compiled top-8 without per-expert norm: ragged rows, 1 to 4 slots per wave, and every
+    # slot local
+    (9, 776, 8, 2, False), (5, 4128, 8, 3, False), (4, 12288, 8, 1, False),
+    (7, 16384, 8, 2, False), (4, 16384, 8, 1, False), (3, 20480, 8, 2, False),
 ])
 def test_ep_partial_matches_oracle(T, H, k, G, pe):
     say(f"ep partial T={T} H={H} k={k} G={G} per_expert={pe}")
