@@ -323,7 +323,7 @@ def launch_config(name: str, d: dict) -> dict:
 
 def cpu_share() -> int:
     """Host threads this process may use: its CPU affinity, capped by OMP_NUM_THREADS when set
-    (a GPU machine allots each GPU a share of the host's cores and says so there)."""
+    (a host shared by several GPUs may allot each GPU a share of its cores and say so there)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:

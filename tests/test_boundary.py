@@ -11,7 +11,7 @@ import finalize_residual_rmsnorm_amd as mf
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mf.h")
 
-# the numbering of the survey's proposed header, with MF_ERR_VALUE and MF_ERR_SCRATCH appended
+# the status numbering include/mf.h declares, MF_ERR_VALUE and MF_ERR_SCRATCH after MF_ERR_HIP
 OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, HIP, VALUE, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 # Fake device addresses: never dereferenced, every call below fails validation first.
