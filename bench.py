@@ -52,7 +52,7 @@ WORKLOAD_CHOICES = ["finalize_prefill", "finalize_1tok", "finalize_1tok_per_expe
                     "gated_residual_next_rmsnorm", "rmsnorm_sigmoid_gate", "moe_route_prefill",
                     "finalize_ep_partial", "finalize_ep_combine", "rmsnorm_mxfp4",
                     "finalize_prefill_mxfp4", "moe_route_decode", "stream_copy",
-                    "stream_copy_per_head", "empty_grid_per_head"]
+                    "stream_copy_per_head", "empty_grid_per_head", "stream_read", "torch_copy"]
 CSRC = os.path.join(ROOT, "finalize_residual_rmsnorm_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -74,6 +74,7 @@ KERNEL_SOURCES = {
     "gated_next": _NORM_SOURCES,
     "per_head": _NORM_SOURCES,
     "copy": _NORM_SOURCES,
+    "read": _NORM_SOURCES,
     "empty_grid": _NORM_SOURCES,
     "route": ["mf_device.h", "route_kernels.h", "api_util.h", "route_api.hip"],
     "rmsnorm_mx": ["mf_device.h", "row_norm.h", "mx_device.h", "mx_kernels.h", "api_util.h",
@@ -143,8 +144,10 @@ def algorithmic_bytes(d: dict) -> int:
     if kind == "per_head":
         n = d["T"] * d["heads"] * d["D"]
         return n * 6 + d["D"] * 2
-    if kind == "copy":
+    if kind in ("copy", "torch_copy"):
         return 2 * d["bytes"]
+    if kind == "read":
+        return d["bytes"] + -(-d["bytes"] // 16384) * 4   # src read; one sink word per 16 KiB
     if kind == "empty_grid":
         return 0
     if kind == "route":
@@ -171,6 +174,11 @@ def make_workload(name: str) -> dict:
     if name == "empty_grid_per_head":
         # an empty kernel of the per-head norm's grid: 8 heads per one-wave workgroup
         return dict(kind="empty_grid", workgroups=4096 * 64 // 8, threads=64)
+    if name == "stream_read":
+        return dict(kind="read", bytes=1 << 30)
+    # PyTorch's own copy of 1 GiB, an outside reference for the copy rate
+    if name == "torch_copy":
+        return dict(kind="torch_copy", bytes=1 << 30)
     return workloads.make_inputs(name)
 
 
@@ -243,10 +251,14 @@ def upload(d: dict, dev):
         x = up(d["x"], True)
         return dict(x=x, gate=up(d["gate"], True), gamma=up(d["gamma"], True),
                     out=torch.empty_like(x))
-    if kind == "copy":
+    if kind in ("copy", "torch_copy"):
         n = d["bytes"] // 4
         return dict(src=torch.randint(0, 1 << 30, (n,), dtype=torch.int32, device=dev),
                     dst=torch.empty(n, dtype=torch.int32, device=dev))
+    if kind == "read":
+        n = d["bytes"] // 4
+        return dict(src=torch.randint(0, 1 << 30, (n,), dtype=torch.int32, device=dev),
+                    sink=torch.empty(-(-d["bytes"] // 16384), dtype=torch.int32, device=dev))
     if kind == "empty_grid":
         return {}
     if kind == "route":
@@ -295,6 +307,10 @@ def launcher(d: dict, g: dict):
                                                   out=g["out"])
     if kind == "copy":
         return lambda: mf.mf_stream_copy(g["src"], g["dst"])
+    if kind == "torch_copy":
+        return lambda: g["dst"].copy_(g["src"])
+    if kind == "read":
+        return lambda: mf.mf_stream_read(g["src"], g["sink"])
     if kind == "empty_grid":
         return lambda: mf.mf_empty_grid(d["workgroups"], d["threads"])
     if kind == "route":

@@ -26,13 +26,15 @@ __all__ = [
     "mf_gated_residual_next_rmsnorm", "mf_gated_residual_next_rmsnorm_supported",
     "mf_moe_finalize_ep_partial", "mf_moe_finalize_ep_combine", "mf_mxfp4_quantize",
     "mf_rmsnorm_mxfp4_quantize", "mf_mxfp4_supported", "mf_moe_finalize_mxfp4", "LIB_PATH",
-    "mf_moe_route_noalloc", "MF_ROUTE_SCRATCH_BYTES", "mf_empty_grid",
+    "mf_moe_route_noalloc", "MF_ROUTE_SCRATCH_BYTES", "mf_empty_grid", "mf_stream_read",
+    "MF_STREAM_READ_CHUNK",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmf.so")
 
 MF_OK = 0
 MF_ROUTE_SCRATCH_BYTES = 4 << 20   # the static scratch of mf_moe_route_noalloc, per GPU
+MF_STREAM_READ_CHUNK = 16384        # bytes of src per word of mf_stream_read's sink
 _lib = None
 
 
@@ -63,6 +65,7 @@ def lib() -> ctypes.CDLL:
             "mf_rmsnorm_sigmoid_gate_supported": [i32],
             "mf_launch_shape": [ci, i64, i32, i32, p, p, p, p],
             "mf_stream_copy": [p, p, i64, p],
+            "mf_stream_read": [p, i64, p, p],
             "mf_empty_grid": [i64, i32, p],
             "mf_status_string": [ci],
             "mf_moe_route": [p, i64, i32, i32, p, p, p, p, p, p, i64, p],
@@ -341,6 +344,26 @@ def mf_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     with _on(src.device):
         _check("mf_stream_copy", lib().mf_stream_copy(src.data_ptr(), dst.data_ptr(), n,
                                                       _stream(stream, src.device)))
+
+
+def mf_stream_read(src: torch.Tensor, sink: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Read src (contiguous, a multiple of 16 bytes) with the library's read kernel; returns the
+    sink: int32 [ceil(bytes / MF_STREAM_READ_CHUNK)], word c the xor of chunk c's 32-bit words."""
+    if src.device.type != "cuda":
+        raise ValueError("mf_stream_read: a GPU tensor required")
+    if not src.is_contiguous():
+        raise ValueError("mf_stream_read: a contiguous tensor required")
+    n = src.numel() * src.element_size()
+    words = -(-n // MF_STREAM_READ_CHUNK)
+    if sink is None:
+        sink = torch.empty(words, dtype=torch.int32, device=src.device)
+    if (sink.device != src.device or sink.dtype != torch.int32 or not sink.is_contiguous()
+            or sink.numel() < words):
+        raise ValueError(f"mf_stream_read: sink must be int32 [{words}] on {src.device}")
+    with _on(src.device):
+        _check("mf_stream_read", lib().mf_stream_read(src.data_ptr(), n, sink.data_ptr(),
+                                                      _stream(stream, src.device)))
+    return sink
 
 
 def mf_empty_grid(workgroups: int, threads: int, device=None, stream=None) -> None:

@@ -180,6 +180,24 @@ int mf_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
                                       reinterpret_cast<hipStream_t>(stream)));
 }
 
+int mf_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+    if (bytes < 0 || bytes % 16 != 0) return MF_ERR_SHAPE;
+    if (bytes == 0) return MF_OK;
+    if (!src || !sink) return MF_ERR_NULL;
+    if (!aligned(src, 16) || !aligned(sink, 4)) return MF_ERR_ALIGN;
+    constexpr int U = 4;
+    const int64_t n = bytes / 16;
+    const int64_t blocks = (n + 256 * U - 1) / (256 * U);
+    static_assert(256 * U * 16 == MF_STREAM_READ_CHUNK, "one workgroup per chunk");
+    if (overlap(src, size_t(bytes), sink, size_t(blocks) * 4)) return MF_ERR_ALIAS;
+    if (!grid_fits(blocks, 256)) return MF_ERR_SHAPE;
+    const u32x4* s = static_cast<const u32x4*>(src);
+    void* args[] = {&s, &sink, const_cast<int64_t*>(&n)};
+    return hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&stream_read_kernel<U>),
+                                      dim3((unsigned)blocks), dim3(256), args, 0,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
 int mf_empty_grid(int64_t workgroups, int32_t threads, void* stream) {
     if (workgroups < 1 || threads < 1 || threads > 1024) return MF_ERR_SHAPE;
     if (!grid_fits(workgroups, threads)) return MF_ERR_SHAPE;

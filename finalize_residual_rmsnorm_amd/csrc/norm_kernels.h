@@ -207,4 +207,31 @@ __global__ void __launch_bounds__(256) stream_copy_kernel(const u32x4* src, u32x
     }
 }
 
+// Streaming read with 16-byte vectors, U vectors in flight per lane (a measurement aid: the HBM
+// read rate with nothing written but one word per chunk).  Each workgroup reads one chunk of
+// 256 * U vectors and writes the xor of its 32-bit words to sink[blockIdx.x].
+template <int U>
+__global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* src, uint32_t* sink, int64_t n) {
+    __shared__ uint32_t part[256 / kWave];
+    const int64_t base = (int64_t)blockIdx.x * (blockDim.x * U) + threadIdx.x;
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t i = base + (int64_t)u * blockDim.x;
+        v[u] = i < n ? ld_stream(src + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+    uint32_t x = 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d /= 2) x ^= uint32_t(__shfl_xor(int(x), d, kWave));
+    if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0u;
+        for (int w = 0; w < int(blockDim.x / kWave); ++w) r ^= part[w];
+        sink[blockIdx.x] = r;
+    }
+}
+
 }  // namespace mf

@@ -290,6 +290,16 @@ int mf_launch_shape(int kind, int64_t T, int32_t H, int32_t k, int32_t* waves_pe
 int mf_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 /*
+ * Streaming read of `bytes` bytes (a multiple of 16; src 16-byte aligned) with the same
+ * 16-byte nontemporal loads.  A measurement aid: it gives the achievable HBM read bandwidth.
+ * Nothing is written but sink[c] = the xor of the 32-bit words of chunk c, for each chunk of
+ * MF_STREAM_READ_CHUNK bytes (the last one may be short): sink holds
+ * ceil(bytes / MF_STREAM_READ_CHUNK) words (4-byte aligned, not overlapping src).
+ */
+#define MF_STREAM_READ_CHUNK 16384
+int mf_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
+/*
  * An empty kernel of `workgroups` workgroups of `threads` threads (1..1024): a measurement aid
  * giving the dispatch floor of a grid shape, e.g. the per-head norm's 32768 one-wave
  * workgroups.  Returns MF_ERR_SHAPE for an empty or oversized grid.

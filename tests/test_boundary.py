@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported():
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     L = ctypes.CDLL(mf.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -245,6 +245,20 @@ def test_stream_copy_rejects_bad_arguments():
     assert L.mf_stream_copy(None, B, 16, None) == NULL
     assert L.mf_stream_copy(A + 8, B, 16, None) == ALIGN
     assert L.mf_stream_copy(A, A + 16, 64, None) == ALIAS
+
+
+def test_stream_read_rejects_bad_arguments():
+    L = mf.lib()
+    assert L.mf_stream_read(A, -16, B, None) == SHAPE
+    assert L.mf_stream_read(A, 24, B, None) == SHAPE
+    assert L.mf_stream_read(A, 0, B, None) == OK
+    assert L.mf_stream_read(None, 16, B, None) == NULL
+    assert L.mf_stream_read(A, 16, None, None) == NULL
+    assert L.mf_stream_read(A + 8, 16, B, None) == ALIGN
+    assert L.mf_stream_read(A, 16, B + 2, None) == ALIGN
+    # the sink (one word per 16 KiB chunk) may not overlap the source
+    assert L.mf_stream_read(A, 3 * 16384, A + 2 * 16384, None) == ALIAS
+    assert L.mf_stream_read(A, 3 * 16384, A + 3 * 16384, None) != ALIAS
 
 
 def test_launch_shapes():

@@ -468,3 +468,16 @@ def test_stream_copy():
     mf.mf_stream_copy(src, dst)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+@pytest.mark.parametrize("nbytes", [16, 16384, 16384 * 5 + 48, 1 << 24])
+def test_stream_read(nbytes):
+    # every chunk's xor of its 32-bit words, checked on the host
+    g = np.random.default_rng(nbytes)
+    host = g.integers(0, 2**32, nbytes // 4, dtype=np.uint32)
+    src = torch.from_numpy(host.view(np.int32)).to(DEV)
+    sink = mf.mf_stream_read(src)
+    torch.cuda.synchronize()
+    chunk = mf.MF_STREAM_READ_CHUNK // 4
+    want = [np.bitwise_xor.reduce(host[i:i + chunk]) for i in range(0, host.size, chunk)]
+    assert np.array_equal(sink.cpu().numpy().view(np.uint32), np.array(want, dtype=np.uint32))
