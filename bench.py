@@ -52,7 +52,8 @@ WORKLOAD_CHOICES = ["finalize_prefill", "finalize_1tok", "finalize_1tok_per_expe
                     "gated_residual_next_rmsnorm", "rmsnorm_sigmoid_gate", "moe_route_prefill",
                     "finalize_ep_partial", "finalize_ep_combine", "rmsnorm_mxfp4",
                     "finalize_prefill_mxfp4", "moe_route_decode", "stream_copy",
-                    "stream_copy_per_head", "empty_grid_per_head", "stream_read", "torch_copy"]
+                    "stream_copy_per_head", "empty_grid_per_head", "stream_read", "torch_copy", "stream_copy_gated",
+                    "stream_copy_rmsnorm_mxfp4"]
 CSRC = os.path.join(ROOT, "finalize_residual_rmsnorm_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -160,8 +161,12 @@ def tokens_of(d: dict) -> int:
     return d["T"] if "T" in d else 0
 
 
-# The per-head norm's bytes (4096 tokens x 64 heads x 64 values: x and gate read, out written)
+# The per-head norm's bytes (4096 tokens x 64 heads x 64 values: x and gate read, out written),
+# the gated-residual norm's (4096 x 8192: x, gate, residual read; residual, out written; gamma)
+# and RMSNorm + MXFP4's (4096 x 8192: x read; codes and scales written; gamma)
 PER_HEAD_BYTES = 4096 * 64 * 64 * 6 + 64 * 2
+GATED_BYTES = 4096 * 8192 * 14 + 8192 * 2
+RMSNORM_MX_BYTES = 4096 * 8192 * 2 + 8192 * 2 + 4096 * 8192 // 2 + 4096 * 8192 // 32
 
 
 def make_workload(name: str) -> dict:
@@ -171,6 +176,10 @@ def make_workload(name: str) -> dict:
     if name == "stream_copy_per_head":
         # a plain copy moving the per-head norm's byte count (half read, half written)
         return dict(kind="copy", bytes=PER_HEAD_BYTES // 2 // 16 * 16)
+    if name == "stream_copy_gated":
+        return dict(kind="copy", bytes=GATED_BYTES // 2 // 16 * 16)
+    if name == "stream_copy_rmsnorm_mxfp4":
+        return dict(kind="copy", bytes=RMSNORM_MX_BYTES // 2 // 16 * 16)
     if name == "empty_grid_per_head":
         # an empty kernel of the per-head norm's grid: 8 heads per one-wave workgroup
         return dict(kind="empty_grid", workgroups=4096 * 64 // 8, threads=64)

@@ -91,3 +91,19 @@ def test_named_finalize_workloads_follow_the_logits_recipe():
     c = bench.oracle_inputs(d)
     assert c["idx"].shape == (64, 8) and c["weights"].dtype == np.float32
     assert np.array_equal(np.sort(c["idx"].ravel()), np.arange(64 * 8))
+
+
+def test_same_size_copies_move_their_norms_bytes():
+    # each copy workload moves exactly the algorithmic bytes of the norm it stands beside, computed
+    # here from small instances of the same formulas scaled to the full sizes
+    import workloads
+    for copy, ref, (T, H) in (("stream_copy_gated", "gated_residual_rmsnorm", (4096, 8192)),
+                              ("stream_copy_rmsnorm_mxfp4", "rmsnorm_mxfp4", (4096, 8192))):
+        small = bench.algorithmic_bytes(workloads.make_inputs(ref, T=1))
+        per_token = bench.algorithmic_bytes(workloads.make_inputs(ref, T=2)) - small
+        full = small + (T - 1) * per_token
+        assert workloads.make_inputs(ref, T=1)["H"] == H
+        assert bench.algorithmic_bytes(bench.make_workload(copy)) == full, copy
+    small = bench.algorithmic_bytes(workloads.make_inputs("rmsnorm_sigmoid_gate", T=1))
+    per_token = bench.algorithmic_bytes(workloads.make_inputs("rmsnorm_sigmoid_gate", T=2)) - small
+    assert bench.algorithmic_bytes(bench.make_workload("stream_copy_per_head")) == small + 4095 * per_token

@@ -164,11 +164,25 @@ def test_rmsnorm_mxfp4_golden():
 
 
 @pytest.mark.parametrize("T,H", [(1, 32), (3, 544), (100, 7168), (7, 32768), (2049, 1024),
-                                 (5, 12288)])
+                                 (5, 12288),
+                                 # 1 to 4 slots per wave over 4 to 8 waves, whole and ragged
+                                 # last slots
+                                 (9, 8192), (5, 4096), (6, 2048), (4, 3072), (3, 4128), (2, 8160),
+                                 (33, 1536), (4097, 8192)])
 def test_rmsnorm_mxfp4_matches_oracle(T, H):
     say(f"rmsnorm mxfp4 T={T} H={H}")
     d = workloads.make_rmsnorm_mx_inputs(T, H, seed=900 + T + H)
     check_rms_mx(d["x"], d["gamma"], d["eps"])
+
+
+@pytest.mark.parametrize("H", [8192, 4128, 12288])
+def test_rmsnorm_mxfp4_batch_invariance(H):
+    # a token's codes and scales do not depend on how many tokens share the launch
+    d = workloads.make_rmsnorm_mx_inputs(301, H, seed=950 + H)
+    say(f"rmsnorm mxfp4 batch invariance H={H}: T=301 against its last 3 tokens alone")
+    q, sc = rms_mx_gpu(d["x"], d["gamma"], d["eps"])
+    q3, sc3 = rms_mx_gpu(d["x"][-3:], d["gamma"], d["eps"])
+    assert np.array_equal(q[-3:], q3) and np.array_equal(sc[-3:], sc3)
 
 
 def test_rmsnorm_mxfp4_workload_full_size():
