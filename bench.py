@@ -53,7 +53,7 @@ WORKLOAD_CHOICES = ["finalize_prefill", "finalize_1tok", "finalize_1tok_per_expe
                     "finalize_ep_partial", "finalize_ep_combine", "rmsnorm_mxfp4",
                     "finalize_prefill_mxfp4", "moe_route_decode", "stream_copy",
                     "stream_copy_per_head", "empty_grid_per_head", "stream_read", "torch_copy", "stream_copy_gated",
-                    "stream_copy_rmsnorm_mxfp4"]
+                    "stream_copy_rmsnorm_mxfp4", "empty_grid_1tok"]
 CSRC = os.path.join(ROOT, "finalize_residual_rmsnorm_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -183,6 +183,9 @@ def make_workload(name: str) -> dict:
     if name == "empty_grid_per_head":
         # an empty kernel of the per-head norm's grid: 8 heads per one-wave workgroup
         return dict(kind="empty_grid", workgroups=4096 * 64 // 8, threads=64)
+    if name == "empty_grid_1tok":
+        # an empty kernel of the one-token finalize's launch: one workgroup of 16 waves
+        return dict(kind="empty_grid", workgroups=1, threads=1024)
     if name == "stream_read":
         return dict(kind="read", bytes=1 << 30)
     # PyTorch's own copy of 1 GiB, an outside reference for the copy rate
