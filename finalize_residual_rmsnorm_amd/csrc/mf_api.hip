@@ -64,12 +64,33 @@ bool uses_wide_kernel(int64_t T, int32_t H, int32_t k, bool per_expert) {
     return s.tail == kRowFull && s.vpl >= 3 && s.vpl <= kWideMaxVpl;
 }
 
+// The finalize without per-expert norm (and its partial and MXFP4 forms): a row of up to 16 slots
+// takes one slot per wave over a power-of-two count of waves, the spare waves idle, rather than
+// the fewest spare slots.  Measured on MI355X (T = 16384, k = 8, one box, interleaved rounds):
+// H = 1536 79.8% of 8 TB/s against 75.9% for 1 wave of 3 slots; 2560 81.3% against 78.1%
+// (2 x 3); 3072 80.8% against 76.2% (2 x 3); 5120 81.3% against 79.0% (4 x 3); 6144 81.1%
+// against 77.7% (4 x 3).  Exactly one wave per slot (3, 5, 6, 10, 12, 14 or 15 waves) came
+// between the two, and below the power of two at H = 7168 (77.1% against 78.7%).
+RowShape plain_finalize_shape(int64_t T, int32_t H) {
+    const int ns = (H + kSlot - 1) / kSlot;
+    if (ns > kMaxWaves) return row_shape(T, H, kMaxWaves, kMaxVpl);
+    RowShape s;
+    s.vpl = 1;
+    s.wpt = pow2_at_least(ns);
+    s.tail = H != ns * kSlot ? kRowRagged : (ns == s.wpt ? kRowFull : kRowWhole);
+    s.block = kWave * s.wpt;
+    s.grid = T;
+    s.nr = 1;
+    s.lds = token_sum_lds_bytes(s.wpt, 1);
+    return s;
+}
+
 // Launch shape of the finalize kernels; `wide` selects the slot-serial kernel's (the bf16-output
 // finalize of wide rows only).
 RowShape finalize_shape(int64_t T, int32_t H, int32_t k, bool per_expert, bool wide = false) {
     if (wide) return wide_shape(T, H);
     RowShape s = per_expert ? row_shape(T, H, kMaxWavesPerExpert, kMaxVplPerExpert)
-                            : row_shape(T, H, kMaxWaves, kMaxVpl);
+                            : plain_finalize_shape(T, H);
     const int kc = k == kCompiledTopK && uses_compiled_topk(s.vpl, per_expert) ? kCompiledTopK : 0;
     s.nr = per_expert ? batch_rows(s.vpl, kc, true) : 1;
     s.lds = token_sum_lds_bytes(s.wpt, s.nr);

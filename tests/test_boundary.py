@@ -277,6 +277,16 @@ def test_launch_shapes():
         waves_per_token=2, vectors_per_lane=1, block=128, grid=16)
     assert mf.mf_launch_shape(mf.KIND_GATED, 4096, 8192) == dict(
         waves_per_token=16, vectors_per_lane=1, block=1024, grid=4096)
+    # the plain finalize: one slot per wave over a power-of-two count of waves up to 16 slots
+    # (6144 = 12 slots: 16 waves, 4 of them spare; 1536: 4 waves, 1 spare; 5000: ragged)
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 9, 6144, 8) == dict(
+        waves_per_token=16, vectors_per_lane=1, block=1024, grid=9)
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 9, 1536, 5) == dict(
+        waves_per_token=4, vectors_per_lane=1, block=256, grid=9)
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 9, 5000, 8)["waves_per_token"] == 16
+    # ... while the gated norm keeps the fewest spare slots (12 slots: 4 waves of 3)
+    assert mf.mf_launch_shape(mf.KIND_GATED, 9, 6144) == dict(
+        waves_per_token=4, vectors_per_lane=3, block=256, grid=9)
     # 12288 = 24 slots: 8 waves of 3 leave no spare slot (16 waves of 2 would leave 8)
     assert mf.mf_launch_shape(mf.KIND_FINALIZE, 5, 12288, 8) == dict(
         waves_per_token=8, vectors_per_lane=3, block=512, grid=5)
