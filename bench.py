@@ -169,8 +169,14 @@ GATED_BYTES = 4096 * 8192 * 14 + 8192 * 2
 RMSNORM_MX_BYTES = 4096 * 8192 * 2 + 8192 * 2 + 4096 * 8192 // 2 + 4096 * 8192 // 32
 
 
-def make_workload(name: str) -> dict:
+def make_workload(name: str, overrides: dict | None = None) -> dict:
+    """A named workload; `overrides` (integer sizes or seed, e.g. {"H": 2048, "k": 4}) change a
+    generated workload's parameters (the measurement aids take none)."""
     import workloads
+    if overrides:
+        if name not in workloads.WORKLOADS:
+            raise ValueError(f"{name} takes no overrides")
+        return workloads.make_inputs(name, **overrides)
     if name == "stream_copy":
         return dict(kind="copy", bytes=1 << 30)
     if name == "stream_copy_per_head":
@@ -593,6 +599,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="finalize_prefill", choices=WORKLOAD_CHOICES)
+    ap.add_argument("--set", action="append", default=[], metavar="KEY=INT",
+                    help="change an integer parameter of the workload (T, H, E, k, seed, ...); "
+                         "repeatable")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (its CPU timing and the sampled parity check)")
     args = ap.parse_args()
@@ -609,7 +618,9 @@ def main() -> int:
     dev = torch.device("cuda:0")
     print(f"# {torch.cuda.get_device_name(dev)}; generating {args.workload}", file=sys.stderr,
           flush=True)
-    d_raw = make_workload(args.workload)
+    overrides = parse_overrides(args.set)
+    d_raw = make_workload(args.workload, overrides)
+    label = args.workload + "".join(f"_{k}{v}" for k, v in overrides.items())
     d = route_on_gpu(d_raw, dev)
     ws = algorithmic_bytes(d)
     # Working sets that fit in the 256 MB Infinity Cache are rotated over enough copies that
@@ -651,7 +662,7 @@ def main() -> int:
     kern_ms = [a.elapsed_time(b) for a, b in ev2]
 
     achieved = ws / avg_kernel_s / 1e9
-    traffic = read_traffic(args.workload, d["kind"]) if d["kind"] in KERNEL_SOURCES else None
+    traffic = read_traffic(label, d["kind"]) if d["kind"] in KERNEL_SOURCES else None
     tokens = tokens_of(d)
     if tokens:
         value, unit = tokens * K / (span_ms / 1e3), "tokens/s"
@@ -661,7 +672,7 @@ def main() -> int:
         value, unit = K / (span_ms / 1e3), "launches/s"
     cfg = {k: d[k] for k in ("T", "H", "E", "k", "heads", "D", "bytes", "workgroups", "threads")
            if k in d}
-    cfg = dict(workload=args.workload, **cfg, routing=_routing(d_raw),
+    cfg = dict(workload=label, **cfg, routing=_routing(d_raw),
                algorithmic_bytes_per_step=ws, input_sets=nsets,
                launch=launch_config(args.workload, d),
                kernel_ms_avg_back_to_back=ms_per_step,
@@ -670,7 +681,7 @@ def main() -> int:
                event_pair_ms_p90=float(np.percentile(kern_ms, 90)),
                host_wall_ms_per_step=wall * 1e3 / K, queue_ran_dry=drained or drained2)
     res = {
-        "metric": METRIC if args.workload == "finalize_prefill" else f"{args.workload} {unit}",
+        "metric": METRIC if label == "finalize_prefill" else f"{label} {unit}",
         "value": value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": cfg,
@@ -684,6 +695,20 @@ def main() -> int:
         res["cpu_baseline"] = cpu_baseline(d_cpu)
     print(json.dumps(res), flush=True)
     return 0 if parity is None or parity["ok"] else 1
+
+
+def parse_overrides(items: list[str]) -> dict:
+    """KEY=INT pairs, in the order given."""
+    out = {}
+    for item in items:
+        key, sep, val = item.partition("=")
+        if not sep or not key.isidentifier():
+            raise SystemExit(f"--set {item!r}: expected KEY=INT")
+        try:
+            out[key] = int(val)
+        except ValueError:
+            raise SystemExit(f"--set {item!r}: {val!r} is not an integer")
+    return out
 
 
 def _routing(d: dict) -> str:

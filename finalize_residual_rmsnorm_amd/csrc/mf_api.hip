@@ -64,20 +64,24 @@ bool uses_wide_kernel(int64_t T, int32_t H, int32_t k, bool per_expert) {
     return s.tail == kRowFull && s.vpl >= 3 && s.vpl <= kWideMaxVpl;
 }
 
-// The finalize without per-expert norm (and its partial and MXFP4 forms): a row of up to 16 slots
-// takes one slot per wave over a power-of-two count of waves, the spare waves idle, rather than
-// the fewest spare slots.  Measured on MI355X (T = 16384, k = 8, one box, interleaved rounds):
-// H = 1536 79.8% of 8 TB/s against 75.9% for 1 wave of 3 slots; 2560 81.3% against 78.1%
-// (2 x 3); 3072 80.8% against 76.2% (2 x 3); 5120 81.3% against 79.0% (4 x 3); 6144 81.1%
-// against 77.7% (4 x 3).  Exactly one wave per slot (3, 5, 6, 10, 12, 14 or 15 waves) came
-// between the two, and below the power of two at H = 7168 (77.1% against 78.7%).
+// The finalize without per-expert norm (and its partial and MXFP4 forms), rather than the fewest
+// spare slots:
+//  - a row of up to 16 slots takes one slot per wave over a power-of-two count of waves, the
+//    spare waves idle.  Measured on MI355X (T = 16384, k = 8, one box, interleaved rounds):
+//    H = 1536 79.8% of 8 TB/s against 75.9% for 1 wave of 3 slots; 2560 81.3% against 78.1%
+//    (2 x 3); 3072 80.8% against 76.2% (2 x 3); 5120 81.3% against 79.0% (4 x 3); 6144 81.1%
+//    against 77.7% (4 x 3).  Exactly one wave per slot (3, 5, 6, 10, 12, 14 or 15 waves) came
+//    between the two, and below the power of two at H = 7168 (77.1% against 78.7%).
+//  - 17 to 32 slots take 8 waves of 3 or 4: at H = 13312, 14336 and 16384 (T = 8192) 75.5%,
+//    75.5% and 74.7% against 73.6%, 74.3% and 73.2% for 16 waves of 2 (one box, every variant
+//    writing the same buffers); 9216 and 10240 at 8 waves of 3 77.8% against 70-72% for 16 x 2.
 RowShape plain_finalize_shape(int64_t T, int32_t H) {
     const int ns = (H + kSlot - 1) / kSlot;
-    if (ns > kMaxWaves) return row_shape(T, H, kMaxWaves, kMaxVpl);
+    if (ns > 2 * kMaxWaves) return row_shape(T, H, kMaxWaves, kMaxVpl);
     RowShape s;
-    s.vpl = 1;
-    s.wpt = pow2_at_least(ns);
-    s.tail = H != ns * kSlot ? kRowRagged : (ns == s.wpt ? kRowFull : kRowWhole);
+    s.vpl = ns > kMaxWaves ? (ns + 7) / 8 : 1;
+    s.wpt = ns > kMaxWaves ? 8 : pow2_at_least(ns);
+    s.tail = H != ns * kSlot ? kRowRagged : (ns == s.wpt * s.vpl ? kRowFull : kRowWhole);
     s.block = kWave * s.wpt;
     s.grid = T;
     s.nr = 1;

@@ -107,3 +107,15 @@ def test_same_size_copies_move_their_norms_bytes():
     small = bench.algorithmic_bytes(workloads.make_inputs("rmsnorm_sigmoid_gate", T=1))
     per_token = bench.algorithmic_bytes(workloads.make_inputs("rmsnorm_sigmoid_gate", T=2)) - small
     assert bench.algorithmic_bytes(bench.make_workload("stream_copy_per_head")) == small + 4095 * per_token
+
+
+def test_workload_overrides():
+    assert bench.parse_overrides(["H=2048", "k=4"]) == {"H": 2048, "k": 4}
+    for bad in (["H"], ["H=2.5"], ["=3"], ["2x=1"]):
+        with pytest.raises(SystemExit):
+            bench.parse_overrides(bad)
+    d = bench.make_workload("finalize_prefill", {"T": 8, "H": 2048, "k": 4})
+    assert (d["T"], d["H"], d["k"], d["E"]) == (8, 2048, 4, 256)
+    assert d["logits"].shape == (8, 256) and d["routing"] == "logits"
+    with pytest.raises(ValueError):
+        bench.make_workload("stream_copy", {"T": 8})

@@ -297,8 +297,13 @@ def test_launch_shapes():
     assert mf.mf_launch_shape(mf.KIND_FINALIZE, 7, 32768, 6) == dict(
         waves_per_token=16, vectors_per_lane=4, block=1024, grid=7)
     assert mf.mf_launch_shape(mf.KIND_FINALIZE, 7, 20480, 8)["vectors_per_lane"] == 5
-    # whole waves of whole slots only: 13312 = 26 slots keeps the batched kernel
-    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 7, 13312, 8)["waves_per_token"] == 16
+    # whole waves of whole slots only: 13312 = 26 slots keeps the batched kernel, at 8 waves of 4
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 7, 13312, 8) == dict(
+        waves_per_token=8, vectors_per_lane=4, block=512, grid=7)
+    # 16384 = 32 slots: 8 waves of 4 (the per-expert variant: its own shape, 8 waves of 4 too)
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 7, 16384, 8)["vectors_per_lane"] == 4
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 7, 10240, 3) == dict(
+        waves_per_token=8, vectors_per_lane=3, block=512, grid=7)
     # the EP combine runs at most 8 waves per token, 16 when 8 waves of 4 slots cannot hold the row
     assert mf.mf_launch_shape(mf.KIND_EP_COMBINE, 2048, 7168) == dict(
         waves_per_token=8, vectors_per_lane=2, block=512, grid=2048)

@@ -222,6 +222,8 @@ def check_finalize_mx(d, rows=None, in_place=False):
     (1, 32, 1, "random"), (17, 1024, 8, "random"), (33, 4128, 9, "random"),
     (100, 7168, 8, "expert_grouped"), (5, 32768, 3, "random"), (64, 4096, 16, "random"),
     (2049, 512, 4, "random"), (7, 12288, 32, "random"), (3, 800, 4, "random"),
+    # 8 waves of 3 or 4 slots, and 16 waves of one slot with spare waves
+    (6, 16384, 8, "random"), (5, 13312, 8, "random"), (9, 6144, 8, "random"),
 ])
 def test_finalize_mxfp4_matches_oracle(T, H, k, layout):
     say(f"finalize mxfp4 T={T} H={H} k={k} layout={layout}")

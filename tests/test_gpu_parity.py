@@ -139,6 +139,10 @@ FINALIZE_SHAPES = [
     (600, 12288, 8, "expert_grouped"), (257, 20480, 8, "random"), (130, 32768, 8, "random"),
     (9, 9216, 8, "random"), (5, 12800, 8, "random"), (7, 12296, 8, "random"),
     (3, 16384, 8, "random"), (11, 24576, 8, "random"), (13, 28672, 8, "random"),
+    # the plain finalize's shapes: one slot per wave over 4, 8 or 16 waves with spare waves
+    # (1536, 3072, 6144), 8 waves of 3 or 4 slots (10240, 13312, 15360 with k = 3)
+    (21, 1536, 8, "random"), (19, 3072, 8, "random"), (17, 6144, 8, "expert_grouped"),
+    (9, 10240, 8, "random"), (8, 13312, 8, "random"), (6, 15360, 3, "random"),
 ]
 
 
