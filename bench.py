@@ -602,6 +602,9 @@ def main() -> int:
     ap.add_argument("--set", action="append", default=[], metavar="KEY=INT",
                     help="change an integer parameter of the workload (T, H, E, k, seed, ...); "
                          "repeatable")
+    ap.add_argument("--sets", type=int, default=0, metavar="N",
+                    help="rotate the timed launches over N copies of the inputs and outputs "
+                         "(default: 1, or enough copies to exceed 1 GiB for small workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (its CPU timing and the sampled parity check)")
     args = ap.parse_args()
@@ -621,11 +624,17 @@ def main() -> int:
     overrides = parse_overrides(args.set)
     d_raw = make_workload(args.workload, overrides)
     label = args.workload + "".join(f"_{k}{v}" for k, v in overrides.items())
+    if args.sets:
+        if args.sets < 1:
+            raise SystemExit("--sets must be at least 1")
+        label += f"_sets{args.sets}"
     d = route_on_gpu(d_raw, dev)
     ws = algorithmic_bytes(d)
     # Working sets that fit in the 256 MB Infinity Cache are rotated over enough copies that
-    # every step reads cold data.
+    # every step reads cold data; --sets fixes the number of copies instead.
     nsets = 1 if ws == 0 or ws >= 4 * MALL_BYTES else min(MAX_INPUT_SETS, -(-4 * MALL_BYTES // ws))
+    if args.sets:
+        nsets = args.sets
     sets = [upload(d, dev) for _ in range(nsets)]
     launches = [launcher(d, g) for g in sets]
     stream = torch.cuda.current_stream(dev)
@@ -673,7 +682,7 @@ def main() -> int:
     cfg = {k: d[k] for k in ("T", "H", "E", "k", "heads", "D", "bytes", "workgroups", "threads")
            if k in d}
     cfg = dict(workload=label, **cfg, routing=_routing(d_raw),
-               algorithmic_bytes_per_step=ws, input_sets=nsets,
+               algorithmic_bytes_per_step=ws, input_sets=nsets, rotated_bytes=ws * nsets,
                launch=launch_config(args.workload, d),
                kernel_ms_avg_back_to_back=ms_per_step,
                event_pair_ms_median=float(np.median(kern_ms)),
