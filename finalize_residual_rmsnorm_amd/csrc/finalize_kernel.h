@@ -289,10 +289,11 @@ moe_finalize_kernel(const FinalizeArgs a) {
 // of a wave is 1 KiB contiguous, free of bank conflicts) and are read back for the residual store
 // and the norm; only the last VPL - NL stay in VGPRs.  At 6 to 8 slots per wave three are staged
 // (52 KiB per workgroup): two 8-wave workgroups per CU, no spills.
-// Measured on MI355X (T = 4096, k = 8, cold, same box, interleaved runs):
-//  - H = 32768: 72.6-73.0% of 8 TB/s against 72.2-72.8% for 16 waves of 4 slots in registers;
-//    H = 28672: 72.6-72.8% against 72.2% for moe_finalize_kernel.
-//  - Not taken: staging at 5 slots for three workgroups per CU at H = 20480 (70.6% against 74.7%),
+// Measured on MI355X (T = 4096, k = 8, cold; one box, interleaved rounds, every variant writing
+// the same output buffers):
+//  - equal within noise to 16 waves of 4 or 3 slots in registers: 71.9% against 72.1% of 8 TB/s at
+//    H = 32768, 72.1% against 72.3% at 24576; at 28672 71.9% against 71.3% for moe_finalize_kernel.
+//  - Not taken: staging at 5 slots for three workgroups per CU at H = 20480 (70.1% against 73.9%),
 //    one staged slot at H = 12288 (71.9% against 77.2%): capped at 80 VGPRs, the waves keep fewer
 //    loads in flight.  Slots interleaved across waves (s * 8 + w, so that the workgroup reads 8 KiB
 //    of each row contiguously at each step): 70.5% at H = 32768.  The residual's loads issued
