@@ -343,7 +343,8 @@ def launch_config(name: str, d: dict) -> dict:
     kind = d["kind"]
     if kind in ("finalize", "ep_partial", "finalize_mx"):
         pe = d.get("expert_gamma") is not None
-        return mf.mf_launch_shape(mf.KIND_FINALIZE_PER_EXPERT if pe else mf.KIND_FINALIZE,
+        plain = mf.KIND_EP_PARTIAL if kind == "ep_partial" else mf.KIND_FINALIZE
+        return mf.mf_launch_shape(mf.KIND_FINALIZE_PER_EXPERT if pe else plain,
                                   d["T"], d["H"], d["k"])
     if kind == "ep_combine":
         return mf.mf_launch_shape(mf.KIND_EP_COMBINE, d["T"], d["H"])

@@ -316,7 +316,7 @@ def mf_rmsnorm_sigmoid_gate_supported(head_dim: int) -> bool:
     return bool(lib().mf_rmsnorm_sigmoid_gate_supported(head_dim))
 
 
-KIND_FINALIZE, KIND_FINALIZE_PER_EXPERT, KIND_GATED, KIND_EP_COMBINE = 0, 1, 2, 3
+KIND_FINALIZE, KIND_FINALIZE_PER_EXPERT, KIND_GATED, KIND_EP_COMBINE, KIND_EP_PARTIAL = 0, 1, 2, 3, 4
 
 
 def mf_launch_shape(kind: int, T: int, H: int, k: int = 1) -> dict:

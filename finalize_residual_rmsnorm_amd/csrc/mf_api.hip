@@ -72,15 +72,20 @@ bool uses_wide_kernel(int64_t T, int32_t H, int32_t k, bool per_expert) {
 //    (2 x 3); 3072 80.8% against 76.2% (2 x 3); 5120 81.3% against 79.0% (4 x 3); 6144 81.1%
 //    against 77.7% (4 x 3).  Exactly one wave per slot (3, 5, 6, 10, 12, 14 or 15 waves) came
 //    between the two, and below the power of two at H = 7168 (77.1% against 78.7%).
+//  - 14 to 16 slots (H = 6657 to 8192) take 8 waves of 2 instead, except in the expert-parallel
+//    partial: the prefill finalize (H = 7168) 480.9-482.3 us against 484.5-486.5 us for 16 waves
+//    of 1 (79.3% against 78.8%, two boxes), H = 8192 0.9% faster, the MXFP4 form 0.2% faster; the
+//    partial 2.5% slower, and 13 slots or fewer equal or slower.
 //  - 17 to 32 slots take 8 waves of 3 or 4: at H = 13312, 14336 and 16384 (T = 8192) 75.5%,
 //    75.5% and 74.7% against 73.6%, 74.3% and 73.2% for 16 waves of 2 (one box, every variant
 //    writing the same buffers); 9216 and 10240 at 8 waves of 3 77.8% against 70-72% for 16 x 2.
-RowShape plain_finalize_shape(int64_t T, int32_t H) {
+RowShape plain_finalize_shape(int64_t T, int32_t H, bool partial) {
     const int ns = (H + kSlot - 1) / kSlot;
     if (ns > 2 * kMaxWaves) return row_shape(T, H, kMaxWaves, kMaxVpl);
+    const bool two = ns > kMaxWaves || (ns >= 14 && !partial);
     RowShape s;
-    s.vpl = ns > kMaxWaves ? (ns + 7) / 8 : 1;
-    s.wpt = ns > kMaxWaves ? 8 : pow2_at_least(ns);
+    s.vpl = ns > kMaxWaves ? (ns + 7) / 8 : (two ? 2 : 1);
+    s.wpt = two ? 8 : pow2_at_least(ns);
     s.tail = H != ns * kSlot ? kRowRagged : (ns == s.wpt * s.vpl ? kRowFull : kRowWhole);
     s.block = kWave * s.wpt;
     s.grid = T;
@@ -90,11 +95,12 @@ RowShape plain_finalize_shape(int64_t T, int32_t H) {
 }
 
 // Launch shape of the finalize kernels; `wide` selects the slot-serial kernel's (the bf16-output
-// finalize of wide rows only).
-RowShape finalize_shape(int64_t T, int32_t H, int32_t k, bool per_expert, bool wide = false) {
+// finalize of wide rows only), `partial` the expert-parallel partial's.
+RowShape finalize_shape(int64_t T, int32_t H, int32_t k, bool per_expert, bool wide = false,
+                        bool partial = false) {
     if (wide) return wide_shape(T, H);
     RowShape s = per_expert ? row_shape(T, H, kMaxWavesPerExpert, kMaxVplPerExpert)
-                            : plain_finalize_shape(T, H);
+                            : plain_finalize_shape(T, H, partial);
     const int kc = k == kCompiledTopK && uses_compiled_topk(s.vpl, per_expert) ? kCompiledTopK : 0;
     s.nr = per_expert ? batch_rows(s.vpl, kc, true) : 1;
     s.lds = token_sum_lds_bytes(s.wpt, s.nr);
@@ -224,19 +230,22 @@ int mf_moe_finalize_supported(int32_t H, int32_t k, int per_expert) {
 
 int mf_launch_shape(int kind, int64_t T, int32_t H, int32_t k, int32_t* waves_per_token,
                     int32_t* vectors_per_lane, int32_t* block_threads, int64_t* grid_blocks) {
-    if (kind < 0 || kind > 3 || T < 0) return MF_ERR_SHAPE;
-    if (kind <= 1 ? !mf_moe_finalize_supported(H, k, kind) : !row_width_supported(H))
+    if (kind < 0 || kind > 4 || T < 0) return MF_ERR_SHAPE;
+    const bool finalize = kind <= 1 || kind == 4;
+    if (finalize ? !mf_moe_finalize_supported(H, k, kind == 1) : !row_width_supported(H))
         return MF_ERR_UNSUPPORTED;
     const bool wide = kind <= 1 && uses_wide_kernel(T, H, k, kind == 1);
     const RowShape s = kind <= 1   ? finalize_shape(T, H, k, kind == 1, wide)
                        : kind == 2 ? row_shape(T, H, kMaxWaves, kMaxVpl)
-                                   : combine_shape(T, H);
+                       : kind == 3 ? combine_shape(T, H)
+                                   : finalize_shape(T, H, k, false, false, true);
     if (T > 0 && !grid_fits(s.grid, s.block)) return MF_ERR_SHAPE;
     // the same kernel lookup as the launch itself
     const void* fn = kind <= 1   ? finalize_kernel_for(s, k, kind == 1, false, wide)
                      : kind == 2 ? gated_kernel_for(s, false)
-                                 : combine_kernel_for(s);
-    if (!fn || (kind <= 1 && s.block > finalize_block_max(kind == 1))) return MF_ERR_UNSUPPORTED;
+                     : kind == 3 ? combine_kernel_for(s)
+                                 : finalize_kernel_for(s, k, false, true);
+    if (!fn || (finalize && s.block > finalize_block_max(kind == 1))) return MF_ERR_UNSUPPORTED;
     if (waves_per_token) *waves_per_token = s.wpt;
     if (vectors_per_lane) *vectors_per_lane = s.vpl;
     if (block_threads) *block_threads = s.block;
@@ -373,7 +382,7 @@ int mf_moe_finalize_ep_partial(const uint16_t* expert_rows, int64_t num_rows,
     const bool per_expert = expert_ids != nullptr || expert_gamma != nullptr;
     if (!mf_moe_finalize_supported(H, k, per_expert)) return MF_ERR_UNSUPPORTED;
     if (T == 0) return MF_OK;
-    const RowShape s = finalize_shape(T, H, k, per_expert);
+    const RowShape s = finalize_shape(T, H, k, per_expert, false, true);
     if (!grid_fits(s.grid, s.block)) return MF_ERR_SHAPE;
     const void* fn = finalize_kernel_for(s, k, per_expert, true);
     if (!fn || s.block > finalize_block_max(per_expert)) return MF_ERR_UNSUPPORTED;

@@ -124,8 +124,8 @@ int mf_moe_finalize_mxfp4(const uint16_t* expert_rows, int64_t num_rows, const i
  *  partials fp32 [num_ranks, T, H] (rank-major), 1 <= num_ranks <= 1024; the other arguments
  *  and their checks as mf_moe_finalize's (residual_out may equal residual).
  * With one rank holding every expert, partial + combine give mf_moe_finalize's residual_out bit
- * for bit, and its out within one bf16 ulp (the combine's final RMSNorm reduces the mean square
- * in another wave layout).
+ * for bit, and its out within one bf16 ulp (the combine's final RMSNorm may reduce the mean
+ * square in another wave layout).
  */
 int mf_moe_finalize_ep_partial(const uint16_t* expert_rows, int64_t num_rows,
                                const int32_t* idx, const float* weights,
@@ -273,11 +273,13 @@ int mf_moe_route_supported(int32_t num_experts, int32_t k);
 int mf_mxfp4_supported(int32_t H);
 
 /*
- * Launch shape that mf_moe_finalize / mf_gated_residual_rmsnorm / mf_moe_finalize_ep_combine
- * use for a problem size: waves per token row, 16-byte vectors per lane (the row slice each
- * lane holds), workgroup size and grid size.  Any output pointer may be NULL.  Returns MF_OK or
- * MF_ERR_UNSUPPORTED.  (kind: 0 = finalize, 1 = finalize with per-expert RMSNorm,
- * 2 = gated-residual RMSNorm, 3 = expert-parallel combine; k is ignored for kinds 2 and 3.)
+ * Launch shape that mf_moe_finalize / mf_gated_residual_rmsnorm / mf_moe_finalize_ep_combine /
+ * mf_moe_finalize_ep_partial use for a problem size: waves per token row, 16-byte vectors per
+ * lane (the row slice each lane holds), workgroup size and grid size.  Any output pointer may be
+ * NULL.  Returns MF_OK or MF_ERR_UNSUPPORTED.  (kind: 0 = finalize, 1 = finalize with
+ * per-expert RMSNorm, 2 = gated-residual RMSNorm, 3 = expert-parallel combine, 4 =
+ * expert-parallel partial without per-expert RMSNorm (with it, kind 1's shape); k is ignored for
+ * kinds 2 and 3.)
  */
 int mf_launch_shape(int kind, int64_t T, int32_t H, int32_t k, int32_t* waves_per_token,
                     int32_t* vectors_per_lane, int32_t* block_threads, int64_t* grid_blocks);

@@ -63,7 +63,10 @@ def test_launch_shape_reported_per_kernel():
                                                        expert_gamma=None))
     assert comb["waves_per_token"] == 8 and comb["vectors_per_lane"] == 2
     assert gated["waves_per_token"] == 16 and gated["vectors_per_lane"] == 1
-    assert fin["waves_per_token"] == 16 and fin["block"] == 1024 and fin["grid"] == 16384
+    assert fin["waves_per_token"] == 8 and fin["block"] == 512 and fin["grid"] == 16384
+    # the EP partial reports its own shape (one slot per wave at H = 7168)
+    part = bench.launch_config("finalize_ep_partial", dict(kind="ep_partial", T=16384, H=7168, k=8))
+    assert part == dict(waves_per_token=16, vectors_per_lane=1, block=1024, grid=16384)
 
 
 def test_cpu_share_and_host_report(monkeypatch):

@@ -264,10 +264,20 @@ def test_stream_read_rejects_bad_arguments():
 def test_launch_shapes():
     # One workgroup per token; its waves (a power of two, at most 16) hold slots of 512
     # values.  The shape depends on H only, never on the token count.
-    # prefill: 14 slots over 16 waves (two spare waves skip their loads)
+    # prefill: 14 slots over 8 waves of 2
     assert mf.mf_launch_shape(mf.KIND_FINALIZE, 16384, 7168, 8) == dict(
+        waves_per_token=8, vectors_per_lane=2, block=512, grid=16384)
+    # ... while the expert-parallel partial keeps one slot per wave there
+    assert mf.mf_launch_shape(mf.KIND_EP_PARTIAL, 16384, 7168, 8) == dict(
         waves_per_token=16, vectors_per_lane=1, block=1024, grid=16384)
+    assert mf.mf_launch_shape(mf.KIND_EP_PARTIAL, 3, 6144, 3) == mf.mf_launch_shape(
+        mf.KIND_FINALIZE, 3, 6144, 3)
+    with pytest.raises(mf.MFError):
+        mf.mf_launch_shape(5, 4, 1024, 2)
     assert mf.mf_launch_shape(mf.KIND_FINALIZE, 3, 7168, 8) == dict(
+        waves_per_token=8, vectors_per_lane=2, block=512, grid=3)
+    # 13 slots (6656): one slot per wave over 16 waves
+    assert mf.mf_launch_shape(mf.KIND_FINALIZE, 3, 6656, 8) == dict(
         waves_per_token=16, vectors_per_lane=1, block=1024, grid=3)
     # decode with per-expert norm: 8 waves
     assert mf.mf_launch_shape(mf.KIND_FINALIZE_PER_EXPERT, 64, 4096, 8) == dict(
@@ -320,7 +330,8 @@ def test_every_supported_width_has_a_kernel():
     for H in range(8, 32768 + 1, 8):
         for kind, k in ((mf.KIND_FINALIZE, 8), (mf.KIND_FINALIZE, 3),
                         (mf.KIND_FINALIZE_PER_EXPERT, 8), (mf.KIND_FINALIZE_PER_EXPERT, 5),
-                        (mf.KIND_GATED, 1), (mf.KIND_EP_COMBINE, 1)):
+                        (mf.KIND_GATED, 1), (mf.KIND_EP_COMBINE, 1), (mf.KIND_EP_PARTIAL, 8),
+                        (mf.KIND_EP_PARTIAL, 2)):
             s = mf.mf_launch_shape(kind, 1000, H, k)
             assert s["waves_per_token"] * s["vectors_per_lane"] * 512 >= H, (kind, H, k)
             assert s["block"] <= (512 if kind == mf.KIND_FINALIZE_PER_EXPERT else 1024)
