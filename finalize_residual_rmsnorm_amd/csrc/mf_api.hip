@@ -37,10 +37,11 @@ RowShape combine_shape(int64_t T, int32_t H) {
 
 // Rows too wide for one or two slots per wave (H > 8192) take the slot-serial kernel
 // (moe_finalize_wide_kernel) at the compiled top-k when its shape fills whole waves of slots:
-// 8 waves per token of 3 or 5 to 8 slots each (H = 12288, 20480, 24576, 28672, 32768; at
-// H = 16384 two slots per wave of 16 waves fit in registers), of which wide_staged_slots wait
-// in LDS.  Other wide shapes (a row that is not whole waves of whole
-// slots, another top-k) keep moe_finalize_kernel.
+// 8 waves per token of 3 or 5 to 8 slots each (H = 12288, 20480, 24576, 28672, 32768), of which
+// wide_staged_slots wait in LDS.  H = 16384, which 16 waves of two slots would fill, keeps
+// moe_finalize_kernel at 8 waves of 4 (74.7% of 8 TB/s against 72.5% for this kernel at that
+// shape, T = 8192), as do the other wide shapes (a row that is not whole waves of whole slots,
+// another top-k).
 constexpr int kWideMaxVpl = 8;
 constexpr int wide_staged_slots(int vpl) { return vpl >= 6 ? 3 : 0; }
 
