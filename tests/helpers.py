@@ -19,14 +19,6 @@ def bf16_ulp_diff(a, b):
     return np.abs(bf16_ordered(a) - bf16_ordered(b))
 
 
-def f32_ulp_diff(a, b):
-    """Distance in float32 units in the last place (+0 == -0)."""
-    def ordered(x):
-        v = np.ascontiguousarray(x, dtype=np.float32).view(np.int32).astype(np.int64)
-        return np.where(v < 0, -(v & 0x7FFFFFFF), v)
-    return np.abs(ordered(a) - ordered(b))
-
-
 def torch_bf16_bits(x):
     """float64/float32 array -> bf16 bit patterns through torch's cast (via float32)."""
     import torch
