@@ -606,6 +606,9 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=0, metavar="N",
                     help="rotate the timed launches over N copies of the inputs and outputs "
                          "(default: 1, or enough copies to exceed 1 GiB for small workloads)")
+    ap.add_argument("--in-place", action="store_true",
+                    help="write residual_out over the residual input (the workloads with a "
+                         "residual: the finalize, its MXFP4 form, the gated norms and the combine)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (its CPU timing and the sampled parity check)")
     args = ap.parse_args()
@@ -624,11 +627,9 @@ def main() -> int:
           flush=True)
     overrides = parse_overrides(args.set)
     d_raw = make_workload(args.workload, overrides)
-    label = args.workload + "".join(f"_{k}{v}" for k, v in overrides.items())
-    if args.sets:
-        if args.sets < 1:
-            raise SystemExit("--sets must be at least 1")
-        label += f"_sets{args.sets}"
+    if args.sets < 0:
+        raise SystemExit("--sets must be at least 1")
+    label = run_label(args.workload, overrides, args.sets, args.in_place)
     d = route_on_gpu(d_raw, dev)
     ws = algorithmic_bytes(d)
     # Working sets that fit in the 256 MB Infinity Cache are rotated over enough copies that
@@ -637,6 +638,11 @@ def main() -> int:
     if args.sets:
         nsets = args.sets
     sets = [upload(d, dev) for _ in range(nsets)]
+    if args.in_place:
+        if not all("res" in g and "res_out" in g for g in sets):
+            raise SystemExit(f"--in-place: {args.workload} has no residual")
+        for g in sets:
+            g["res_out"] = g["res"]
     launches = [launcher(d, g) for g in sets]
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
@@ -684,6 +690,7 @@ def main() -> int:
            if k in d}
     cfg = dict(workload=label, **cfg, routing=_routing(d_raw),
                algorithmic_bytes_per_step=ws, input_sets=nsets, rotated_bytes=ws * nsets,
+               residual_in_place=args.in_place,
                launch=launch_config(args.workload, d),
                kernel_ms_avg_back_to_back=ms_per_step,
                event_pair_ms_median=float(np.median(kern_ms)),
@@ -705,6 +712,17 @@ def main() -> int:
         res["cpu_baseline"] = cpu_baseline(d_cpu)
     print(json.dumps(res), flush=True)
     return 0 if parity is None or parity["ok"] else 1
+
+
+def run_label(workload: str, overrides: dict, sets: int = 0, in_place: bool = False) -> str:
+    """The name a run's JSON line and profile summaries carry: the workload, then any size
+    overrides, the number of rotated input sets and the in-place residual, in that order."""
+    label = workload + "".join(f"_{k}{v}" for k, v in overrides.items())
+    if sets:
+        label += f"_sets{sets}"
+    if in_place:
+        label += "_inplace"
+    return label
 
 
 def parse_overrides(items: list[str]) -> dict:

@@ -122,3 +122,13 @@ def test_workload_overrides():
     assert d["logits"].shape == (8, 256) and d["routing"] == "logits"
     with pytest.raises(ValueError):
         bench.make_workload("stream_copy", {"T": 8})
+
+
+def test_run_labels():
+    # the names under which runs and their profile summaries are kept
+    assert bench.run_label("finalize_prefill", {}) == "finalize_prefill"
+    assert bench.run_label("finalize_prefill", {"H": 4096, "k": 2}) == "finalize_prefill_H4096_k2"
+    assert bench.run_label("finalize_prefill", {"T": 20480}, 2) == "finalize_prefill_T20480_sets2"
+    assert bench.run_label("finalize_prefill", {}, 0, True) == "finalize_prefill_inplace"
+    assert (bench.run_label("gated_residual_rmsnorm", {"T": 64}, 3, True)
+            == "gated_residual_rmsnorm_T64_sets3_inplace")
