@@ -143,6 +143,8 @@ FINALIZE_SHAPES = [
     # (1536, 3072, 6144), 8 waves of 3 or 4 slots (10240, 13312, 15360 with k = 3)
     (21, 1536, 8, "random"), (19, 3072, 8, "random"), (17, 6144, 8, "expert_grouped"),
     (9, 10240, 8, "random"), (8, 13312, 8, "random"), (6, 15360, 3, "random"),
+    # the largest row and the largest top-k together, and the largest top-k with a ragged row
+    (2, 32768, 64, "random"), (3, 4104, 64, "expert_grouped"),
 ]
 
 
@@ -297,11 +299,12 @@ def test_finalize_decode_per_expert_workload():
 
 
 @pytest.mark.parametrize("T,H,k", [(1, 64, 1), (5, 520, 3), (33, 7168, 8), (2100, 7168, 8),
-                                   (3, 4096, 13), (9, 32768, 2), (2500, 1024, 4), (5, 3848, 8)])
+                                   (3, 4096, 13), (9, 32768, 2), (2500, 1024, 4), (5, 3848, 8),
+                                   (2, 2048, 64), (2, 32768, 8)])
 def test_per_expert_matches_oracle(T, H, k):
     say(f"per-expert T={T} H={H} k={k}: {shape_str(1, T, H, k)}")
-    d = workloads.make_finalize_inputs(T, H, E=32, k=k, seed=2000 + T + H + k, per_expert=True,
-                                       residual_std=2.0)
+    d = workloads.make_finalize_inputs(T, H, E=max(32, k), k=k, seed=2000 + T + H + k,
+                                       per_expert=True, residual_std=2.0)
     out, r = finalize_gpu(d, per_expert=True)
     torch.cuda.synchronize()
     r_ref, o_ref = finalize_ref(d, per_expert=True)
