@@ -289,7 +289,7 @@ moe_finalize_kernel(const FinalizeArgs a) {
 // of a wave is 1 KiB contiguous, free of bank conflicts) and are read back for the residual store
 // and the norm; only the last VPL - NL stay in VGPRs.  At 6 to 8 slots per wave three are staged
 // (52 KiB per workgroup): two 8-wave workgroups per CU, no spills.
-// Measured on MI355X (T = 4096, k = 8, cold; one box, interleaved rounds, every variant writing
+// Measured on MI355X (T = 4096, k = 8, cold; one GPU, interleaved rounds, every variant writing
 // the same output buffers):
 //  - equal within noise to 16 waves of 4 or 3 slots in registers: 71.9% against 72.1% of 8 TB/s at
 //    H = 32768, 72.1% against 72.3% at 24576; at 28672 71.9% against 71.3% for moe_finalize_kernel.

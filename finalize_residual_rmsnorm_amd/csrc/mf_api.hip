@@ -68,17 +68,17 @@ bool uses_wide_kernel(int64_t T, int32_t H, int32_t k, bool per_expert) {
 // The finalize without per-expert norm (and its partial and MXFP4 forms), rather than the fewest
 // spare slots:
 //  - a row of up to 16 slots takes one slot per wave over a power-of-two count of waves, the
-//    spare waves idle.  Measured on MI355X (T = 16384, k = 8, one box, interleaved rounds):
+//    spare waves idle.  Measured on MI355X (T = 16384, k = 8, one GPU, interleaved rounds):
 //    H = 1536 79.8% of 8 TB/s against 75.9% for 1 wave of 3 slots; 2560 81.3% against 78.1%
 //    (2 x 3); 3072 80.8% against 76.2% (2 x 3); 5120 81.3% against 79.0% (4 x 3); 6144 81.1%
 //    against 77.7% (4 x 3).  Exactly one wave per slot (3, 5, 6, 10, 12, 14 or 15 waves) came
 //    between the two, and below the power of two at H = 7168 (77.1% against 78.7%).
 //  - 14 to 16 slots (H = 6657 to 8192) take 8 waves of 2 instead, except in the expert-parallel
 //    partial: the prefill finalize (H = 7168) 480.9-482.3 us against 484.5-486.5 us for 16 waves
-//    of 1 (79.3% against 78.8%, two boxes), H = 8192 0.9% faster, the MXFP4 form 0.2% faster; the
+//    of 1 (79.3% against 78.8%, on two GPUs), H = 8192 0.9% faster, the MXFP4 form 0.2% faster; the
 //    partial 2.5% slower, and 13 slots or fewer equal or slower.
 //  - 17 to 32 slots take 8 waves of 3 or 4: at H = 13312, 14336 and 16384 (T = 8192) 75.5%,
-//    75.5% and 74.7% against 73.6%, 74.3% and 73.2% for 16 waves of 2 (one box, every variant
+//    75.5% and 74.7% against 73.6%, 74.3% and 73.2% for 16 waves of 2 (one GPU, every variant
 //    writing the same buffers); 9216 and 10240 at 8 waves of 3 77.8% against 70-72% for 16 x 2.
 RowShape plain_finalize_shape(int64_t T, int32_t H, bool partial) {
     const int ns = (H + kSlot - 1) / kSlot;
