@@ -168,15 +168,14 @@ int mf_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
     if (!src || !dst) return MF_ERR_NULL;
     if (!aligned(src, 16) || !aligned(dst, 16)) return MF_ERR_ALIGN;
     if (overlap(src, size_t(bytes), dst, size_t(bytes))) return MF_ERR_ALIAS;
-    constexpr int U = 4;
     const int64_t n = bytes / 16;
-    const int64_t blocks = (n + 256 * U - 1) / (256 * U);
-    if (!grid_fits(blocks, 256)) return MF_ERR_SHAPE;
+    const int64_t blocks = (n + kCopyBlock - 1) / kCopyBlock;
+    if (!grid_fits(blocks, kCopyBlock)) return MF_ERR_SHAPE;
     const u32x4* s = static_cast<const u32x4*>(src);
     u32x4* d = static_cast<u32x4*>(dst);
     void* args[] = {&s, &d, const_cast<int64_t*>(&n)};
-    return hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&stream_copy_kernel<U>),
-                                      dim3((unsigned)blocks), dim3(256), args, 0,
+    return hip_status(hipLaunchKernel(reinterpret_cast<const void*>(&stream_copy_kernel),
+                                      dim3((unsigned)blocks), dim3(kCopyBlock), args, 0,
                                       reinterpret_cast<hipStream_t>(stream)));
 }
 

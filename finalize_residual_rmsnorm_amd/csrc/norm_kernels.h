@@ -190,35 +190,37 @@ __global__ void __launch_bounds__(kPerHeadBlock) rmsnorm_sigmoid_gate_kernel(con
 __global__ void empty_grid_kernel() {}
 
 // ---------------------------------------------------------------------------------------
-// Streaming copy with 16-byte vectors, U vectors in flight per lane.
-template <int U>
-__global__ void __launch_bounds__(256) stream_copy_kernel(const u32x4* src, u32x4* dst, int64_t n) {
-    const int64_t base = (int64_t)blockIdx.x * (blockDim.x * U) + threadIdx.x;
-    u32x4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t i = base + (int64_t)u * blockDim.x;
-        if (i < n) v[u] = ld_stream(src + i);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t i = base + (int64_t)u * blockDim.x;
-        if (i < n) st_stream(v[u], dst + i);
-    }
+// Streaming copy: one 16-byte vector per lane, one wave per workgroup (kCopyBlock threads).
+// Measured on MI355X, cold, the fastest simple copy at every size tried: 83.7% of 8 TB/s for
+// 2 GiB moved, against 81.2% with 256-thread workgroups and 77.5% with four vectors per lane in
+// 256-thread workgroups; 82.5% at 470 MB, 73.6% at 101 MB, 71.8% at 85 MB (3-8 points above
+// the others).
+constexpr int kCopyBlock = 64;
+__global__ void __launch_bounds__(kCopyBlock) stream_copy_kernel(const u32x4* src, u32x4* dst, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * kCopyBlock + threadIdx.x;
+    if (i < n) st_stream(ld_stream(src + i), dst + i);
 }
 
 // Streaming read with 16-byte vectors, U vectors in flight per lane (a measurement aid: the HBM
 // read rate with nothing written but one word per chunk).  Each workgroup reads one chunk of
 // 256 * U vectors and writes the xor of its 32-bit words to sink[blockIdx.x].
+// A chunk wholly inside the source is read with no per-vector test: guarding each load
+// separately made the compiler wait for every other load before issuing the next.
 template <int U>
 __global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* src, uint32_t* sink, int64_t n) {
     __shared__ uint32_t part[256 / kWave];
-    const int64_t base = (int64_t)blockIdx.x * (blockDim.x * U) + threadIdx.x;
+    const int64_t chunk = (int64_t)blockDim.x * U;
+    const int64_t base = (int64_t)blockIdx.x * chunk + threadIdx.x;
     u32x4 v[U];
+    if ((int64_t)(blockIdx.x + 1) * chunk <= n) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t i = base + (int64_t)u * blockDim.x;
-        v[u] = i < n ? ld_stream(src + i) : u32x4{0u, 0u, 0u, 0u};
+        for (int u = 0; u < U; ++u) v[u] = ld_stream(src + base + (int64_t)u * blockDim.x);
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + (int64_t)u * blockDim.x;
+            v[u] = i < n ? ld_stream(src + i) : u32x4{0u, 0u, 0u, 0u};
+        }
     }
     uint32_t x = 0u;
 #pragma unroll

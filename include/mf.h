@@ -285,9 +285,11 @@ int mf_launch_shape(int kind, int64_t T, int32_t H, int32_t k, int32_t* waves_pe
                     int32_t* vectors_per_lane, int32_t* block_threads, int64_t* grid_blocks);
 
 /*
- * Streaming copy of `bytes` bytes (a multiple of 16; both pointers 16-byte aligned) with the
- * same 16-byte vector loads and stores as the kernels above.  A measurement aid: it gives
- * the achievable HBM copy bandwidth and calibrates the HBM byte counters.
+ * Streaming copy of `bytes` bytes (a multiple of 16, at most 64 GiB; both pointers 16-byte
+ * aligned, not overlapping) with the same 16-byte nontemporal loads and stores as the kernels
+ * above, one per lane in one-wave workgroups.  A measurement aid: it gives the achievable HBM
+ * copy bandwidth and calibrates the HBM byte counters.  MF_ERR_SHAPE for a bad or oversized
+ * byte count.
  */
 int mf_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
 

@@ -245,6 +245,8 @@ def test_stream_copy_rejects_bad_arguments():
     assert L.mf_stream_copy(None, B, 16, None) == NULL
     assert L.mf_stream_copy(A + 8, B, 16, None) == ALIGN
     assert L.mf_stream_copy(A, A + 16, 64, None) == ALIAS
+    # one vector per lane in one-wave workgroups: at most 2^32 lanes, 64 GiB
+    assert L.mf_stream_copy(A, A + (1 << 40), (64 << 30) + 16, None) == SHAPE
 
 
 def test_stream_read_rejects_bad_arguments():
