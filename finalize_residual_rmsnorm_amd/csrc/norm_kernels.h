@@ -131,11 +131,12 @@ gated_residual_rmsnorm_kernel(const GatedArgs a) {
 // TAIL = false is the full-tile kernel (the head count is a multiple of 8: no clamp, no
 // predicate); TAIL = true also handles a last wave whose heads end inside it, with the same
 // arithmetic on every head that exists (bit-identical to the full-tile kernel there).
-// Measured on MI355X at 4096 tokens x 64 heads (cold inputs): the kernel runs in 16.8-17.0 us,
-// faster than a plain copy of the same 100.7 MB (18.6 us), while an empty kernel of the same
-// 32768 one-wave workgroups already takes 8.1 us to dispatch.  Issuing the gate load only after
-// the x load has returned measured 1% faster than issuing both at once; 4-wave workgroups (5%)
-// and persistent waves that prefetch their next group (11%) measured slower.
+// Measured on MI355X at 4096 tokens x 64 heads (cold inputs): the kernel runs in 16.7-17.1 us,
+// 96-99% of the rate of stream_copy_kernel moving the same 100.7 MB (16.5 us), while an empty
+// kernel of the same 32768 one-wave workgroups already takes 7.7 us to dispatch.  Issuing the
+// gate load only after the x load has returned measured 1% faster than issuing both at once;
+// 4-wave workgroups (5%) and persistent waves that prefetch their next group (11%) measured
+// slower.
 struct PerHeadArgs {
     const uint16_t* x;      // bf16 [T*heads, 64]
     const uint16_t* gate;   // bf16 [T*heads, 64]
