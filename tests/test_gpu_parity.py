@@ -469,12 +469,16 @@ def test_per_head_ragged(T, heads):
 # ----------------------------------------------------------------------------- copy
 
 
-def test_stream_copy():
-    src = torch.randint(-2**31, 2**31 - 1, (1 << 20,), dtype=torch.int32, device=DEV)
-    dst = torch.zeros_like(src)
-    mf.mf_stream_copy(src, dst)
+@pytest.mark.parametrize("nbytes", [16, 1040, 1 << 22, (1 << 22) + 48])
+def test_stream_copy(nbytes):
+    # whole and partial last workgroups; the bytes past the copy stay untouched
+    n = nbytes // 4
+    src = torch.randint(-2**31, 2**31 - 1, (n + 16,), dtype=torch.int32, device=DEV)
+    dst = torch.full((n + 16,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    mf.mf_stream_copy(src[:n], dst[:n])
     torch.cuda.synchronize()
-    assert torch.equal(src, dst)
+    assert torch.equal(src[:n], dst[:n])
+    assert bool((dst[n:] == 0x5A5A5A5A).all())
 
 
 @pytest.mark.parametrize("nbytes", [16, 16384, 16384 * 5 + 48, 1 << 24])
