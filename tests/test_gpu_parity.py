@@ -160,6 +160,48 @@ def test_finalize_matches_oracle(T, H, k, layout):
     assert_bf16_close(bits(out), o_ref)
 
 
+def _random_finalize_cases(n=24, n_wide=8, seed=20261203):
+    """Seeded random shapes across the launch-shape rules, each small enough for the oracle
+    (T * k * H <= 8e6): n with H a multiple of 8 from 8 to 32768 (log-uniform), k from 1 to 64
+    and T from 1 to 300; then n_wide rows wider than 8192 (every other one a whole number of
+    4 KiB, with k = 8 on every other one: the slot-serial kernel's shapes among them), k up to 16.
+    Random and expert-grouped layouts alternate; every third case is per-expert."""
+    g = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n + n_wide:
+        i = len(cases)
+        if i < n:
+            H = 8 * int(np.exp(g.uniform(0.0, np.log(4096.0))))
+            k = int(np.exp(g.uniform(0.0, np.log(64.0))))
+            T = int(g.integers(1, 301))
+        else:
+            H = 8 * int(g.integers(1025, 4097)) if i % 2 else 2048 * int(g.integers(5, 17))
+            k = 8 if (i // 2) % 2 else int(g.integers(1, 17))
+            T = int(g.integers(1, 41))
+        if T * k * H > 8_000_000:
+            continue
+        cases.append((T, H, k, ("random", "expert_grouped")[i % 2], i % 3 == 2))
+    return cases
+
+
+@pytest.mark.parametrize("T,H,k,layout,per_expert", _random_finalize_cases())
+def test_finalize_random_shapes(T, H, k, layout, per_expert):
+    say(f"finalize random shape T={T} H={H} k={k} {layout} per_expert={per_expert}: "
+        f"{shape_str(int(per_expert), T, H, k)}")
+    d = workloads.make_finalize_inputs(T, H, E=max(16, k), k=k, seed=5000 + T + H + k,
+                                       layout=layout, per_expert=per_expert)
+    out, r = finalize_gpu(d, per_expert=per_expert)
+    torch.cuda.synchronize()
+    r_ref, o_ref = finalize_ref(d, per_expert=per_expert)
+    rg = r.cpu().numpy()
+    if per_expert:
+        assert_fp32_tol(rg, r_ref, min_exact=0.5)
+        assert_out_given_residual(bits(out), rg, d["gamma"], d["eps"], o_ref)
+    else:
+        assert np.array_equal(rg, r_ref)
+        assert_bf16_close(bits(out), o_ref)
+
+
 @pytest.fixture(scope="module")
 def prefill():
     say("generating the prefill workload T=16384 H=7168 E=256 k=8 (host, ~20 s)")
