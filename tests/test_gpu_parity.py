@@ -508,6 +508,72 @@ def test_per_head_ragged(T, heads):
     assert_bf16_close(bits(out), o_ref, min_exact=0.98)
 
 
+# ----------------------------------------------------------------------------- random shapes
+
+
+def _random_norm_cases(n=12, seed=20261204):
+    """Seeded random (T, H) for the gated norms: H a multiple of 8 from 8 to 32768 (log-uniform),
+    T from 1 to 3000, T * H <= 4e6."""
+    g = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        H = 8 * int(np.exp(g.uniform(0.0, np.log(4096.0))))
+        T = int(np.exp(g.uniform(0.0, np.log(3000.0))))
+        if T * H <= 4_000_000:
+            cases.append((T, H))
+    return cases
+
+
+def _floor(n_elements, floor):
+    # a bit-identical fraction is only asserted where there are enough elements for it to be
+    # stable; the ulp and tolerance bars hold everywhere
+    return floor if n_elements >= 4096 else 0.0
+
+
+@pytest.mark.parametrize("T,H", _random_norm_cases())
+def test_gated_random_shapes(T, H):
+    say(f"gated random shape T={T} H={H}: {shape_str(2, T, H)}")
+    d = workloads.make_gated_inputs(T, H, seed=6000 + T + H)
+    out, r = gated_gpu(d)
+    torch.cuda.synchronize()
+    r_ref, o_ref = oracle.gated_residual_rmsnorm(d["x"], d["gate"], d["residual"], d["gamma"],
+                                                 d["eps"])
+    rg = r.cpu().numpy()
+    assert_fp32_tol(rg, r_ref, min_exact=_floor(T * H, GATED_MIN_EXACT))
+    want = refs.rmsnorm_of(rg, d["gamma"], d["eps"])
+    assert_bf16_close(bits(out), want, min_exact=_floor(T * H, 0.99))
+
+
+@pytest.mark.parametrize("T,H", _random_norm_cases(n=8, seed=20261205))
+def test_gated_next_random_shapes(T, H):
+    say(f"gated dual random shape T={T} H={H}: {shape_str(2, T, H)}")
+    d = workloads.make_gated_inputs(T, H, seed=7000 + T + H, dual=True)
+    out, on, r = gated_next_gpu(d)
+    torch.cuda.synchronize()
+    r_ref, _, _ = oracle.gated_residual_next_rmsnorm(
+        d["x"], d["gate"], d["residual"], d["gamma"], d["gamma_next"], d["eps"])
+    rg = r.cpu().numpy()
+    assert_fp32_tol(rg, r_ref, min_exact=_floor(T * H, GATED_MIN_EXACT))
+    for o, gm in ((out, d["gamma"]), (on, d["gamma_next"])):
+        assert_bf16_close(bits(o), refs.rmsnorm_of(rg, gm, d["eps"]), min_exact=_floor(T * H, 0.99))
+
+
+def _random_per_head_cases(n=12, seed=20261206):
+    g = np.random.default_rng(seed)
+    return [(int(np.exp(g.uniform(0.0, np.log(3000.0)))), int(g.integers(1, 129))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("T,heads", _random_per_head_cases())
+def test_per_head_random_shapes(T, heads):
+    say(f"per-head random shape T={T} heads={heads}")
+    d = workloads.make_per_head_inputs(T, heads, 64, seed=8000 + T + heads)
+    out = mf.mf_rmsnorm_sigmoid_gate(up(d["x"], True), up(d["gate"], True), up(d["gamma"], True),
+                                     d["eps"])
+    torch.cuda.synchronize()
+    o_ref = oracle.rmsnorm_sigmoid_gate(d["x"], d["gate"], d["gamma"], d["eps"])
+    assert_bf16_close(bits(out), o_ref, min_exact=_floor(T * heads * 64, 0.99))
+
+
 # ----------------------------------------------------------------------------- copy
 
 
