@@ -129,6 +129,46 @@ def test_ep_combine_matches_oracle(T, H, G):
     assert_bf16_close(bits(out), o_ref)
 
 
+def _random_ep_cases(n, seed, partial):
+    """Seeded random shapes: H a multiple of 8 from 8 to 32768 (log-uniform); the partial with k
+    from 1 to 16 (every other case the compiled 8) and 1 to 8 ranks, every third case per-expert;
+    the combine with 1 to 16 ranks.  Each small enough for the oracle."""
+    g = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        H = 8 * int(np.exp(g.uniform(0.0, np.log(4096.0))))
+        T = int(np.exp(g.uniform(0.0, np.log(400.0))))
+        if partial:
+            k = 8 if len(cases) % 2 else int(g.integers(1, 17))
+            G = int(g.integers(1, 9))
+            if T * k * H <= 6_000_000:
+                cases.append((T, H, k, G, len(cases) % 3 == 2))
+        else:
+            G = int(g.integers(1, 17))
+            if T * G * H <= 8_000_000:
+                cases.append((T, H, G))
+    return cases
+
+
+@pytest.mark.parametrize("T,H,k,G,pe", _random_ep_cases(12, 20261207, True))
+def test_ep_partial_random_shapes(T, H, k, G, pe):
+    test_ep_partial_matches_oracle(T, H, k, G, pe)
+
+
+@pytest.mark.parametrize("T,H,G", _random_ep_cases(10, 20261208, False))
+def test_ep_combine_random_shapes(T, H, G):
+    say(f"ep combine random shape T={T} H={H} G={G}")
+    d = workloads.make_ep_combine_inputs(T, H, G, seed=730 + T + H + G)
+    out, r = mf.mf_moe_finalize_ep_combine(up(d["partials"]), up(d["residual"]),
+                                           up(d["gamma"], True), d["eps"])
+    torch.cuda.synchronize()
+    r_ref, o_ref = oracle.moe_finalize_ep_combine(d["partials"], d["residual"], d["gamma"],
+                                                  d["eps"])
+    assert np.array_equal(r.cpu().numpy(), r_ref)
+    # (the bit-identical fraction is asserted only where there are enough elements for it)
+    assert_bf16_close(bits(out), o_ref, min_exact=0.99 if T * H >= 4096 else 0.0)
+
+
 def test_ep_combine_in_place():
     d = workloads.make_ep_combine_inputs(100, 7168, 8, seed=730)
     say("ep combine in place: T=100 H=7168 G=8")

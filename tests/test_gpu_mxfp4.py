@@ -121,15 +121,15 @@ def nearest(r):
     return np.where(np.signbit(r), -E2M1[pick], E2M1[pick])
 
 
-def check_rms_mx(x, gamma, eps):
+def check_rms_mx(x, gamma, eps, min_exact=0.999):
     q, sc = rms_mx_gpu(x, gamma, eps)
     q_ref, sc_ref = oracle.rmsnorm_mxfp4_quantize(x, gamma, eps)
-    check_band(q, sc, q_ref, sc_ref, workloads.bf16_bits_to_f32(x), gamma, eps)
+    check_band(q, sc, q_ref, sc_ref, workloads.bf16_bits_to_f32(x), gamma, eps, min_exact)
 
 
-def check_band(q, sc, q_ref, sc_ref, xf, gamma, eps):
+def check_band(q, sc, q_ref, sc_ref, xf, gamma, eps, min_exact=0.999):
     """q, sc from the GPU against the oracle's (q_ref, sc_ref) for the RMSNorm of the fp32 rows
-    xf with gamma: the band bar of the module docstring."""
+    xf with gamma: the band bar of the module docstring (the bit-identical floor min_exact)."""
     T, H = xf.shape
     # the oracle's fp32 normalised value, and a band around it
     xd = xf.astype(np.float64)
@@ -148,7 +148,7 @@ def check_band(q, sc, q_ref, sc_ref, xf, gamma, eps):
     ok = (dec >= np.minimum(v1, v2)) & (dec <= np.maximum(v1, v2))
     assert ok.all(), f"{(~ok).sum()} codes outside the band"
     exact = ((q == q_ref).sum() + (sc == sc_ref).sum()) / (q.size + sc.size)
-    assert exact >= 0.999, f"bit-identical fraction {exact:.5f}"
+    assert exact >= min_exact, f"bit-identical fraction {exact:.5f}"
     say(f"    bit-identical fraction {exact:.6f}")
 
 
@@ -208,14 +208,14 @@ def finalize_mx_gpu(d, in_place=False):
     return q.cpu().numpy(), sc.cpu().numpy(), r.cpu().numpy()
 
 
-def check_finalize_mx(d, rows=None, in_place=False):
+def check_finalize_mx(d, rows=None, in_place=False, min_exact=0.999):
     q, sc, r = finalize_mx_gpu(d, in_place)
     sel = slice(None) if rows is None else rows
     r_ref, _ = oracle.moe_finalize(d["expert_rows"], d["idx"][sel], d["weights"][sel],
                                    d["residual"][sel], d["gamma"], d["eps"])
     assert np.array_equal(r[sel].view(np.uint32), r_ref.view(np.uint32)), "residual_out differs"
     q_ref, sc_ref = oracle.rmsnorm_f32_mxfp4_quantize(r_ref, d["gamma"], d["eps"])
-    check_band(q[sel], sc[sel], q_ref, sc_ref, r_ref, d["gamma"], d["eps"])
+    check_band(q[sel], sc[sel], q_ref, sc_ref, r_ref, d["gamma"], d["eps"], min_exact)
 
 
 @pytest.mark.parametrize("T,H,k,layout", [
@@ -230,6 +230,44 @@ def test_finalize_mxfp4_matches_oracle(T, H, k, layout):
     d = workloads.make_finalize_inputs(T, H, E=max(16, k), k=k, seed=950 + T + H + k,
                                        layout=layout)
     check_finalize_mx(d)
+
+
+def _random_mx_cases(n, seed, finalize):
+    """Seeded random shapes: H a multiple of 32 from 32 to 32768 (log-uniform), T up to 400; the
+    finalize with k from 1 to 16 (every other case the compiled 8).  Each small enough for the
+    oracle."""
+    g = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        H = 32 * int(np.exp(g.uniform(0.0, np.log(1024.0))))
+        T = int(np.exp(g.uniform(0.0, np.log(400.0))))
+        if finalize:
+            k = 8 if len(cases) % 2 else int(g.integers(1, 17))
+            if T * k * H <= 6_000_000:
+                cases.append((T, H, k, ("random", "expert_grouped")[len(cases) % 2]))
+        elif T * H <= 4_000_000:
+            cases.append((T, H))
+    return cases
+
+
+def _mx_floor(T, H):
+    # the bit-identical floor only where there are enough code and scale bytes for it
+    return 0.999 if T * (H // 2 + H // 32) >= 4096 else 0.0
+
+
+@pytest.mark.parametrize("T,H,k,layout", _random_mx_cases(10, 20261209, True))
+def test_finalize_mxfp4_random_shapes(T, H, k, layout):
+    say(f"finalize mxfp4 random shape T={T} H={H} k={k} layout={layout}")
+    d = workloads.make_finalize_inputs(T, H, E=max(16, k), k=k, seed=970 + T + H + k,
+                                       layout=layout)
+    check_finalize_mx(d, min_exact=_mx_floor(T, H))
+
+
+@pytest.mark.parametrize("T,H", _random_mx_cases(10, 20261210, False))
+def test_rmsnorm_mxfp4_random_shapes(T, H):
+    say(f"rmsnorm mxfp4 random shape T={T} H={H}")
+    d = workloads.make_rmsnorm_mx_inputs(T, H, seed=980 + T + H)
+    check_rms_mx(d["x"], d["gamma"], d["eps"], min_exact=_mx_floor(T, H))
 
 
 def test_finalize_mxfp4_in_place():
