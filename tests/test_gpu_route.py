@@ -110,6 +110,25 @@ def test_route_shapes(T, E, k, q):
     check_route(d["logits"], k, "route shape")
 
 
+def _random_route_cases(n=12, seed=20261211):
+    """Seeded random (T, E, k, bf16-valued logits): T from 1 to 20000 and E from 1 to 1024
+    (log-uniform), k from 1 to min(E, 16)."""
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        T = int(np.exp(g.uniform(0.0, np.log(20000.0))))
+        E = int(np.exp(g.uniform(0.0, np.log(1024.0))))
+        k = int(g.integers(1, min(E, 16) + 1))
+        cases.append((T, E, k, i % 2 == 1))
+    return cases
+
+
+@pytest.mark.parametrize("T,E,k,q", _random_route_cases())
+def test_route_random_shapes(T, E, k, q):
+    d = workloads.make_route_inputs(T, E, k, seed=450 + T + E + k, bf16_logits=q)
+    check_route(d["logits"], k, "route random shape")
+
+
 def test_route_special_values():
     # every logit equal (all ties), signed zeros, -inf entries and huge magnitudes
     E, k = 96, 8
