@@ -161,6 +161,57 @@ def test_per_head_guard_bands(T, heads):
     check_all(g, dict(out=out))
 
 
+# ----------------------------------------------------------------------------- random shapes
+
+
+def _random_rows(n, seed, with_k):
+    """Seeded random ragged shapes: H a multiple of 8 from 8 to 32768 (log-uniform), T from 1 to
+    64, and with_k a top-k from 1 to 64 (every third case per-expert)."""
+    g = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        H = 8 * int(np.exp(g.uniform(0.0, np.log(4096.0))))
+        T = int(g.integers(1, 65))
+        if not with_k:
+            cases.append((T, H))
+            continue
+        k = int(np.exp(g.uniform(0.0, np.log(64.0))))
+        if T * k * H <= 4_000_000:
+            cases.append((T, H, k, len(cases) % 3 == 2))
+    return cases
+
+
+@pytest.mark.parametrize("T,H,k,pe", _random_rows(16, 20261212, True))
+def test_finalize_guard_bands_random_shapes(T, H, k, pe):
+    say(f"guard bands finalize random shape T={T} H={H} k={k} per_expert={pe}")
+    d = workloads.make_finalize_inputs(T, H, E=max(16, k), k=k, seed=1150 + T + H + k,
+                                       per_expert=pe, layout="random")
+    kw = dict(expert_ids=up(d["expert_ids"]), expert_gamma=up(d["expert_gamma"], True)) if pe else {}
+    args = (up(d["expert_rows"], True), up(d["idx"]), up(d["weights"]), up(d["residual"]),
+            up(d["gamma"], True), d["eps"])
+    out, r = mf.mf_moe_finalize(*args, **kw)
+    g = guarded(out=((T, H), torch.bfloat16), r=((T, H), torch.float32))
+    mf.mf_moe_finalize(*args, residual_out=g["r"].view, out=g["out"].view, **kw)
+    check_all(g, dict(out=out, r=r))
+
+
+@pytest.mark.parametrize("T,H", _random_rows(10, 20261213, False))
+def test_gated_guard_bands_random_shapes(T, H):
+    say(f"guard bands gated random shape T={T} H={H}")
+    d = workloads.make_gated_inputs(T, H, seed=1550 + T + H)
+    args = (up(d["x"], True), up(d["gate"], True), up(d["residual"]), up(d["gamma"], True), d["eps"])
+    out, r = mf.mf_gated_residual_rmsnorm(*args)
+    g = guarded(out=((T, H), torch.bfloat16), r=((T, H), torch.float32))
+    mf.mf_gated_residual_rmsnorm(*args, residual_out=g["r"].view, out=g["out"].view)
+    check_all(g, dict(out=out, r=r))
+
+
+@pytest.mark.parametrize("T,heads", [(int(t), int(h)) for t, h in
+                                     np.random.default_rng(20261214).integers(1, 97, (8, 2))])
+def test_per_head_guard_bands_random_shapes(T, heads):
+    test_per_head_guard_bands(T, heads)
+
+
 # ----------------------------------------------------------------------------- MXFP4
 
 
